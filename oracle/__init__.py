@@ -1,0 +1,145 @@
+"""CPU oracle for the CSR graph-attention path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and its
+binding) never does.
+
+``oracle.c`` holds the plain double-precision definitions (see its header for
+the page passages each follows); this module compiles it with gcc and wraps it
+with ctypes.  ``binning.py`` is the plain CPU statement of the degree binning.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+
+
+def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP over independent rows)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", *extra_flags, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"unsupported feature dtype {a.dtype}")
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes wrapper around one compiled oracle library (the real one, or a test mutant)."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            if path != LIB:
+                raise FileNotFoundError(path)
+            build()
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        L = self.lib
+        L.oracle_num_threads.restype = i32
+        L.oracle_sddmm.argtypes = [i64, vp, vp, vp, vp, i32, i32, i32, dbl, vp]
+        L.oracle_edge_softmax.argtypes = [i64, vp, i32, vp, vp]
+        L.oracle_aggregate.argtypes = [i64, vp, vp, i32, i32, vp, vp, i32, vp]
+        L.oracle_softmax_aggregate.argtypes = [i64, vp, vp, i32, i32, vp, vp, i32, vp]
+        L.oracle_layer.argtypes = [i64, vp, vp, i32, i32, vp, vp, vp, i32, dbl, vp]
+        for f in (L.oracle_sddmm, L.oracle_edge_softmax, L.oracle_aggregate,
+                  L.oracle_softmax_aggregate, L.oracle_layer):
+            f.restype = i32
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    # --- steps -------------------------------------------------------------------------
+    def sddmm(self, src_idx, dst_idx, src_feat, dst_feat, scale: float = 1.0) -> np.ndarray:
+        src_idx = np.ascontiguousarray(src_idx, np.int32)
+        dst_idx = np.ascontiguousarray(dst_idx, np.int32)
+        src_feat = np.ascontiguousarray(src_feat)
+        dst_feat = np.ascontiguousarray(dst_feat)
+        assert src_feat.dtype == dst_feat.dtype and src_feat.ndim == 3 and dst_feat.ndim == 3
+        H, D = src_feat.shape[1:]
+        assert dst_feat.shape[1:] == (H, D)
+        out = np.empty((src_idx.size, H), np.float64)
+        rc = self.lib.oracle_sddmm(src_idx.size, _p(src_idx), _p(dst_idx), _p(src_feat), _p(dst_feat),
+                                   _dtype_code(src_feat), H, D, float(scale), _p(out))
+        assert rc == 0
+        return out
+
+    def edge_softmax(self, row_ptr, scores) -> np.ndarray:
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        scores = np.ascontiguousarray(scores, np.float64)
+        E, H = scores.shape
+        assert row_ptr[-1] == E
+        out = np.full((E, H), np.nan, np.float64)
+        rc = self.lib.oracle_edge_softmax(row_ptr.size - 1, _p(row_ptr), H, _p(scores), _p(out))
+        assert rc == 0
+        return out
+
+    def aggregate(self, row_ptr, col_idx, weights, feat) -> np.ndarray:
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        col_idx = np.ascontiguousarray(col_idx, np.int32)
+        weights = np.ascontiguousarray(weights, np.float64)
+        feat = np.ascontiguousarray(feat)
+        H, D = feat.shape[1:]
+        n = row_ptr.size - 1
+        out = np.full((n, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_aggregate(n, _p(row_ptr), _p(col_idx), H, D, _p(weights), _p(feat),
+                                       _dtype_code(feat), _p(out))
+        assert rc == 0
+        return out
+
+    def softmax_aggregate(self, row_ptr, col_idx, scores, feat) -> np.ndarray:
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        col_idx = np.ascontiguousarray(col_idx, np.int32)
+        scores = np.ascontiguousarray(scores, np.float64)
+        feat = np.ascontiguousarray(feat)
+        H, D = feat.shape[1:]
+        n = row_ptr.size - 1
+        out = np.full((n, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_softmax_aggregate(n, _p(row_ptr), _p(col_idx), H, D, _p(scores), _p(feat),
+                                               _dtype_code(feat), _p(out))
+        assert rc == 0
+        return out
+
+    def layer(self, row_ptr, col_idx, q, k, v, scale: float = 1.0) -> np.ndarray:
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        col_idx = np.ascontiguousarray(col_idx, np.int32)
+        q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+        assert q.dtype == k.dtype == v.dtype
+        H, D = v.shape[1:]
+        n = row_ptr.size - 1
+        assert q.shape[0] == n
+        out = np.full((n, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_layer(n, _p(row_ptr), _p(col_idx), H, D, _p(q), _p(k), _p(v),
+                                   _dtype_code(v), float(scale), _p(out))
+        assert rc == 0
+        return out
+
+
+_default = None
+
+
+def get() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

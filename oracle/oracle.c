@@ -1,0 +1,192 @@
+/*
+ * CPU oracle for the CSR graph-attention path.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  It is the plain definition of every step, written as
+ * per-row / per-edge loops in double precision, so that a reader can check it
+ * against the definitions by eye.  It shares no code, header or helper with the
+ * HIP library; neither side includes or calls the other.
+ *
+ * Sources of the definitions (POPCORNBENCH kernel-writing transcripts):
+ *   [l1_p10] edge-only SDDMM: the reference model gathers src_feat[src_idx]
+ *            and dst_feat[dst_idx] and sums their product over the feature dim.
+ *   [l1_p6]  multi-head row-wise softmax over CSR edge scores: the reference
+ *            loops over nodes and applies a softmax over the edge slice
+ *            scores[row_ptr[i]:row_ptr[i+1], h] for every head, computed as
+ *            exp(x - max) / sum(exp(x - max)).
+ *   [l1_p18] multi-head sparse aggregation: out[i,h,:] is the sum over the
+ *            row's edges of edge_weight[e,h] * node_feat[col_idx[e],h,:];
+ *            the output starts from zeros.
+ *   [l2_p37] CSR neighbourhood attention: softmax of the row's edge scores,
+ *            then the weighted sum of node_value[col_idx[e]]; rows with no edges
+ *            keep their zero output.
+ * The full layer (scores from q_i . k_j, then softmax, then aggregation of v)
+ * is the composition of the three steps above; no single page writes it out.
+ *
+ * Precision: every floating-point input is widened exactly to double (bf16 is
+ * decoded bit-exactly) and all arithmetic is double; results are returned as
+ * double.  Outer loops over independent rows / edges may run on several
+ * threads (OpenMP); that does not change any result.
+ *
+ * Pins (tests/test_oracle_pins.py): dense brute force with library matmul and
+ * softmax on tiny graphs (with edge multiplicities), closed forms (degree-1
+ * rows, constant scores, two-edge logistic), invariants (rows sum to one,
+ * shift invariance, zero rows give +0.0, linearity, edge permutation within a
+ * row), exact integer arithmetic, and mutation runs showing that planted
+ * mistakes in this file fail at least one pin.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_F64 2
+
+/* Element idx of a feature table stored as fp32, bf16 (raw bits) or fp64, widened exactly. */
+static double load_feat(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return ((const double*)base)[idx];
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+#else
+    return 1;
+#endif
+}
+
+/*
+ * SDDMM over an edge list [l1_p10]:
+ *   out[e,h] = scale * sum_d dst_feat[dst_idx[e],h,d] * src_feat[src_idx[e],h,d]
+ * Features are [n,heads,head_dim] row-major; out is [n_edges,heads].
+ */
+int oracle_sddmm(int64_t n_edges, const int32_t* src_idx, const int32_t* dst_idx,
+                 const void* src_feat, const void* dst_feat, int dtype,
+                 int heads, int head_dim, double scale, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n_edges; ++e) {
+        for (int h = 0; h < heads; ++h) {
+            int64_t a = ((int64_t)dst_idx[e] * heads + h) * head_dim;
+            int64_t b = ((int64_t)src_idx[e] * heads + h) * head_dim;
+            double acc = 0.0;
+            for (int d = 0; d < head_dim; ++d)
+                acc += load_feat(dst_feat, dtype, a + d) * load_feat(src_feat, dtype, b + d);
+            out[e * heads + h] = scale * acc;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Row-wise multi-head edge softmax [l1_p6]: for every row i with at least one
+ * edge and every head h, over e in [row_ptr[i], row_ptr[i+1]):
+ *   m = max_e s[e,h];  z = sum_e exp(s[e,h] - m);  out[e,h] = exp(s[e,h] - m) / z
+ * Rows without edges have no entries.  scores/out are [n_edges,heads].
+ */
+int oracle_edge_softmax(int64_t n_rows, const int32_t* row_ptr, int heads,
+                        const double* scores, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t start = row_ptr[i], end = row_ptr[i + 1];
+        if (end <= start) continue;
+        for (int h = 0; h < heads; ++h) {
+            double m = -INFINITY;
+            for (int64_t e = start; e < end; ++e)
+                if (scores[e * heads + h] > m) m = scores[e * heads + h];
+            double z = 0.0;
+            for (int64_t e = start; e < end; ++e)
+                z += exp(scores[e * heads + h] - m);
+            for (int64_t e = start; e < end; ++e)
+                out[e * heads + h] = exp(scores[e * heads + h] - m) / z;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Weighted neighbour aggregation (SpMM) [l1_p18]:
+ *   out[i,h,d] = sum_{e in row i} weights[e,h] * feat[col_idx[e],h,d]
+ * starting from 0.0, so rows without edges are +0.0.  out is [n_rows,heads,head_dim].
+ */
+int oracle_aggregate(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                     int heads, int head_dim, const double* weights,
+                     const void* feat, int dtype, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t start = row_ptr[i], end = row_ptr[i + 1];
+        for (int h = 0; h < heads; ++h) {
+            for (int d = 0; d < head_dim; ++d) {
+                double acc = 0.0;
+                for (int64_t e = start; e < end; ++e)
+                    acc += weights[e * heads + h] *
+                           load_feat(feat, dtype, ((int64_t)col_idx[e] * heads + h) * head_dim + d);
+                out[(i * heads + h) * head_dim + d] = acc;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Neighbourhood softmax + aggregation [l2_p37]: aggregate(softmax(scores)).
+ * The edge weights are materialised in a temporary [n_edges,heads] buffer.
+ */
+int oracle_softmax_aggregate(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                             int heads, int head_dim, const double* scores,
+                             const void* feat, int dtype, double* out)
+{
+    int64_t n_edges = row_ptr[n_rows];
+    double* alpha = (double*)malloc((size_t)(n_edges > 0 ? n_edges : 1) * heads * sizeof(double));
+    if (!alpha) return 1;
+    oracle_edge_softmax(n_rows, row_ptr, heads, scores, alpha);
+    oracle_aggregate(n_rows, row_ptr, col_idx, heads, head_dim, alpha, feat, dtype, out);
+    free(alpha);
+    return 0;
+}
+
+/*
+ * Full layer: scores[e,h] = scale * <q[i,h,:], k[col_idx[e],h,:]> for every edge
+ * e of row i (the SDDMM with dst = row, src = column), then softmax +
+ * aggregation of v.  q is [n_rows,heads,head_dim]; k and v are [n_src,heads,head_dim].
+ */
+int oracle_layer(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                 int heads, int head_dim, const void* q, const void* k, const void* v,
+                 int dtype, double scale, double* out)
+{
+    int64_t n_edges = row_ptr[n_rows];
+    size_t ne = (size_t)(n_edges > 0 ? n_edges : 1);
+    int32_t* dst = (int32_t*)malloc(ne * sizeof(int32_t));
+    double* scores = (double*)malloc(ne * heads * sizeof(double));
+    if (!dst || !scores) { free(dst); free(scores); return 1; }
+    for (int64_t i = 0; i < n_rows; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e)
+            dst[e] = (int32_t)i;
+    oracle_sddmm(n_edges, col_idx, dst, k, q, dtype, heads, head_dim, scale, scores);
+    int rc = oracle_softmax_aggregate(n_rows, row_ptr, col_idx, heads, head_dim, scores, v, dtype, out);
+    free(dst);
+    free(scores);
+    return rc;
+}

@@ -1,0 +1,291 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError on failure.
+They compare against: dense brute force with library routines (numpy matmul,
+scipy softmax) on tiny graphs, closed forms, invariants, and exact integer
+arithmetic.  ``tests/test_oracle_pins.py`` runs them on the real oracle, and on
+mutants of ``oracle/oracle.c`` with planted mistakes (each must fail a pin).
+
+Run as ``python tests/oracle_pins.py <liboracle.so>``: exit status = number of
+failing pins (used for the mutants, in a child process).
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import scipy.special
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from sparse_graph_attention_degree_amd import graphs as G  # noqa: E402
+
+
+def _rng(s):
+    return np.random.default_rng(s)
+
+
+def _graph(seed, n=9, ns=7, max_deg=6, dup=True, zero_frac=0.2):
+    g = G.random_csr(n, ns, max_deg, _rng(seed), zero_frac=zero_frac, duplicates=dup)
+    if (g.degrees() == 0).sum() == 0:  # make sure a zero row is present
+        deg = g.degrees().copy()
+        deg[n // 2] = 0
+        g = G.csr_from_degrees(deg, ns, _rng(seed + 1000))
+    return g
+
+
+def _multiplicity(g):
+    C = np.zeros((g.n_rows, g.n_src))
+    rows = G.row_of_edge(g.row_ptr)
+    np.add.at(C, (rows, g.col_idx), 1.0)
+    return C
+
+
+# ------------------------------------------------------------------------------- SDDMM
+def pin_sddmm_dense(orc):
+    """out[e,h] == scale * (Dst_h @ Src_h^T)[dst[e], src[e]] for fp64 / fp32 / bf16 tables."""
+    r = _rng(1)
+    for H, D in [(1, 4), (3, 16), (2, 8)]:
+        ns, nd, E = 7, 5, 40
+        src_idx = r.integers(0, ns, E).astype(np.int32)
+        dst_idx = r.integers(0, nd, E).astype(np.int32)
+        for dt in ("f64", "f32", "bf16"):
+            A = r.standard_normal((nd, H, D))
+            B = r.standard_normal((ns, H, D))
+            if dt == "f64":
+                Af, Bf, Ain, Bin = A, B, A, B
+            elif dt == "f32":
+                Ain, Bin = A.astype(np.float32), B.astype(np.float32)
+                Af, Bf = Ain.astype(np.float64), Bin.astype(np.float64)
+            else:
+                Ain, Bin = G.f32_to_bf16_bits(A.astype(np.float32)), G.f32_to_bf16_bits(B.astype(np.float32))
+                Af, Bf = G.bf16_bits_to_f32(Ain).astype(np.float64), G.bf16_bits_to_f32(Bin).astype(np.float64)
+            got = orc.sddmm(src_idx, dst_idx, Bin, Ain, scale=0.75)
+            for h in range(H):
+                dense = Af[:, h, :] @ Bf[:, h, :].T
+                np.testing.assert_allclose(got[:, h], 0.75 * dense[dst_idx, src_idx], rtol=1e-12, atol=1e-12)
+
+
+def pin_sddmm_integer_exact(orc):
+    """Integer-valued features in [-8, 8]: every dot product is exact, so equality is bitwise."""
+    r = _rng(2)
+    H, D, ns, nd, E = 2, 128, 11, 13, 64
+    A = r.integers(-8, 9, (nd, H, D)).astype(np.float32)
+    B = r.integers(-8, 9, (ns, H, D)).astype(np.float32)
+    src_idx = r.integers(0, ns, E).astype(np.int32)
+    dst_idx = r.integers(0, nd, E).astype(np.int32)
+    got = orc.sddmm(src_idx, dst_idx, G.f32_to_bf16_bits(B), G.f32_to_bf16_bits(A))
+    want = np.stack([(A[:, h].astype(np.int64) @ B[:, h].T.astype(np.int64))[dst_idx, src_idx] for h in range(H)], 1)
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+# ------------------------------------------------------------------------------- softmax
+def pin_softmax_closed_forms(orc):
+    """deg-1 row -> 1 exactly; constant row -> 1/deg; two edges (0, t) -> logistic; zero row -> no entries."""
+    deg = [1, 5, 2, 0, 1]
+    rp = G.row_ptr_from_degrees(deg)
+    H = 2
+    t = np.array([0.7, -3.25])
+    s = np.zeros((rp[-1], H))
+    s[0] = [3.0, -40.0]                 # deg 1
+    s[1:6] = [[2.5, -1.0]] * 5          # constant
+    s[6] = [0.0, 0.0]
+    s[7] = t                            # two edges: (0, t)
+    s[8] = [-7.0, 123.0]                # deg 1
+    a = orc.edge_softmax(rp, s)
+    assert np.array_equal(a[0], [1.0, 1.0]) and np.array_equal(a[8], [1.0, 1.0])
+    np.testing.assert_allclose(a[1:6], 0.2, rtol=1e-15)
+    np.testing.assert_allclose(a[6], 1.0 / (1.0 + np.exp(t)), rtol=1e-14)
+    np.testing.assert_allclose(a[7], np.exp(t) / (1.0 + np.exp(t)), rtol=1e-14)
+
+
+def pin_softmax_dense(orc):
+    """Duplicate-free graphs: scipy softmax over the dense row with -inf off the edge set."""
+    for seed, H in [(3, 1), (4, 4)]:
+        g = _graph(seed, n=12, ns=10, max_deg=8, dup=False)
+        s = _rng(seed).standard_normal((g.n_edges, H)) * 3
+        a = orc.edge_softmax(g.row_ptr, s)
+        rows = G.row_of_edge(g.row_ptr)
+        for h in range(H):
+            S = np.full((g.n_rows, g.n_src), -np.inf)
+            S[rows, g.col_idx] = s[:, h]
+            nz = g.degrees() > 0
+            P = np.zeros_like(S)
+            P[nz] = scipy.special.softmax(S[nz], axis=1)
+            np.testing.assert_allclose(a[:, h], P[rows, g.col_idx], rtol=1e-12, atol=1e-15)
+
+
+def pin_softmax_invariants(orc):
+    """Rows sum to 1 per head; a per-(row, head) shift leaves the result unchanged, also for
+    shifts of +-1000 where an unstabilised exp over/underflows."""
+    g = _graph(5, n=20, ns=15, max_deg=12)
+    H = 3
+    s = _rng(5).standard_normal((g.n_edges, H)) * 2
+    a = orc.edge_softmax(g.row_ptr, s)
+    rows = G.row_of_edge(g.row_ptr)
+    sums = np.zeros((g.n_rows, H))
+    np.add.at(sums, rows, a)
+    nz = g.degrees() > 0
+    np.testing.assert_allclose(sums[nz], 1.0, rtol=1e-13)
+    for big in (0.0, 1000.0, -1000.0):
+        c = _rng(6).standard_normal((g.n_rows, H)) * 5 + big
+        a2 = orc.edge_softmax(g.row_ptr, s + c[rows])
+        np.testing.assert_allclose(a2, a, rtol=1e-10, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------- aggregate
+def pin_aggregate_dense(orc):
+    """out[:,h,:] == W_h @ X[:,h,:] with W_h[i,j] = sum of weights of the i->j edges (duplicates add)."""
+    for seed, (H, D), dt in [(7, (1, 4), "f64"), (8, (3, 8), "f32"), (9, (2, 16), "bf16")]:
+        g = _graph(seed, n=10, ns=8, max_deg=9, dup=True)
+        w = _rng(seed).standard_normal((g.n_edges, H))
+        X = _rng(seed + 1).standard_normal((g.n_src, H, D))
+        if dt == "f32":
+            Xin = X.astype(np.float32)
+            X = Xin.astype(np.float64)
+        elif dt == "bf16":
+            Xin = G.f32_to_bf16_bits(X.astype(np.float32))
+            X = G.bf16_bits_to_f32(Xin).astype(np.float64)
+        else:
+            Xin = X
+        out = orc.aggregate(g.row_ptr, g.col_idx, w, Xin)
+        rows = G.row_of_edge(g.row_ptr)
+        for h in range(H):
+            W = np.zeros((g.n_rows, g.n_src))
+            np.add.at(W, (rows, g.col_idx), w[:, h])
+            np.testing.assert_allclose(out[:, h, :], W @ X[:, h, :], rtol=1e-12, atol=1e-12)
+
+
+def pin_aggregate_integer_exact(orc):
+    """Integer weights and features: sums are exact, compare bitwise with an int64 dense product."""
+    g = _graph(10, n=16, ns=12, max_deg=10)
+    H, D = 2, 16
+    w = _rng(10).integers(-4, 5, (g.n_edges, H)).astype(np.float64)
+    X = _rng(11).integers(-8, 9, (g.n_src, H, D)).astype(np.float32)
+    out = orc.aggregate(g.row_ptr, g.col_idx, w, X)
+    rows = G.row_of_edge(g.row_ptr)
+    for h in range(H):
+        W = np.zeros((g.n_rows, g.n_src), np.int64)
+        np.add.at(W, (rows, g.col_idx), w[:, h].astype(np.int64))
+        assert np.array_equal(out[:, h, :], (W @ X[:, h, :].astype(np.int64)).astype(np.float64))
+
+
+def pin_zero_rows_positive_zero(orc):
+    """Rows without edges give +0.0 (sign bit clear) from aggregate, softmax+aggregate and layer."""
+    g = _graph(12, n=14, ns=9, max_deg=5, zero_frac=0.4)
+    H, D = 2, 4
+    z = g.degrees() == 0
+    assert z.any()
+    w = _rng(12).standard_normal((g.n_edges, H))
+    X = _rng(13).standard_normal((g.n_src, H, D))
+    q = _rng(14).standard_normal((g.n_rows, H, D))
+    for out in (orc.aggregate(g.row_ptr, g.col_idx, w, X),
+                orc.softmax_aggregate(g.row_ptr, g.col_idx, w, X),
+                orc.layer(g.row_ptr, g.col_idx, q, X, X)):
+        assert np.all(out[z] == 0.0) and not np.any(np.signbit(out[z]))
+
+
+# ------------------------------------------------------------------------------- fused
+def _dense_masked_softmax_v(C, S, V):
+    """Dense softmax over each row's edge multiset: P = C*exp(S - m) / sum(C*exp(S - m)), out = P @ V."""
+    out = np.zeros((C.shape[0], V.shape[1]))
+    for i in range(C.shape[0]):
+        mask = C[i] > 0
+        if not mask.any():
+            continue
+        m = S[i, mask].max()
+        wts = np.where(mask, C[i] * np.exp(np.where(mask, S[i] - m, 0.0)), 0.0)
+        out[i] = (wts / wts.sum()) @ V
+    return out
+
+
+def pin_softmax_aggregate_dense(orc):
+    """Scores that depend only on (i, j): dense masked softmax (with multiplicities) times V."""
+    for seed, (H, D) in [(15, (1, 8)), (16, (4, 4))]:
+        g = _graph(seed, n=11, ns=9, max_deg=10, dup=True)
+        rows = G.row_of_edge(g.row_ptr)
+        S = _rng(seed).standard_normal((H, g.n_rows, g.n_src)) * 2
+        s = np.stack([S[h][rows, g.col_idx] for h in range(H)], 1)
+        X = _rng(seed + 1).standard_normal((g.n_src, H, D))
+        out = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, X)
+        C = _multiplicity(g)
+        for h in range(H):
+            np.testing.assert_allclose(out[:, h, :], _dense_masked_softmax_v(C, S[h], X[:, h, :]),
+                                       rtol=1e-12, atol=1e-13)
+
+
+def pin_softmax_aggregate_closed_forms(orc):
+    """deg-1 row gives its source row exactly; constant features give that constant;
+    the result is linear in the features and invariant to permuting a row's edges."""
+    g = _graph(17, n=16, ns=10, max_deg=7)
+    H, D = 2, 8
+    s = _rng(17).standard_normal((g.n_edges, H)) * 2
+    X = _rng(18).standard_normal((g.n_src, H, D))
+    Y = _rng(19).standard_normal((g.n_src, H, D))
+    out = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, X)
+    deg = g.degrees()
+    for i in np.flatnonzero(deg == 1):
+        assert np.array_equal(out[i], X[g.col_idx[g.row_ptr[i]]])
+    const = np.broadcast_to(np.array([1.5, -2.25])[None, :, None], (g.n_src, H, D)).copy()
+    oc = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, const)
+    np.testing.assert_allclose(oc[deg > 0], np.broadcast_to(const[0], oc[deg > 0].shape), rtol=1e-14)
+    lin = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, 2.0 * X - 3.0 * Y)
+    oy = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, Y)
+    np.testing.assert_allclose(lin, 2.0 * out - 3.0 * oy, rtol=1e-12, atol=1e-12)
+    # permute edges inside every row (scores move with their edges)
+    perm = np.arange(g.n_edges)
+    r = _rng(20)
+    for i in range(g.n_rows):
+        b, e = g.row_ptr[i], g.row_ptr[i + 1]
+        perm[b:e] = b + r.permutation(e - b)
+    op = orc.softmax_aggregate(g.row_ptr, g.col_idx[perm], s[perm], X)
+    np.testing.assert_allclose(op, out, rtol=1e-12, atol=1e-13)
+
+
+def pin_layer_dense(orc):
+    """Full layer vs dense softmax(mask_C o scale*Q K^T) V per head, fp64 and bf16 tables."""
+    for seed, (H, D), dt in [(21, (2, 8), "f64"), (22, (4, 16), "bf16")]:
+        g = _graph(seed, n=10, ns=12, max_deg=9, dup=True)
+        Q = _rng(seed).standard_normal((g.n_rows, H, D))
+        K = _rng(seed + 1).standard_normal((g.n_src, H, D))
+        V = _rng(seed + 2).standard_normal((g.n_src, H, D))
+        if dt == "bf16":
+            Qi, Ki, Vi = (G.f32_to_bf16_bits(a.astype(np.float32)) for a in (Q, K, V))
+            Q, K, V = (G.bf16_bits_to_f32(a).astype(np.float64) for a in (Qi, Ki, Vi))
+        else:
+            Qi, Ki, Vi = Q, K, V
+        scale = 0.25
+        out = orc.layer(g.row_ptr, g.col_idx, Qi, Ki, Vi, scale=scale)
+        C = _multiplicity(g)
+        for h in range(H):
+            S = scale * (Q[:, h, :] @ K[:, h, :].T)
+            np.testing.assert_allclose(out[:, h, :], _dense_masked_softmax_v(C, S, V[:, h, :]),
+                                       rtol=1e-11, atol=1e-12)
+
+
+ALL_PINS = [pin_sddmm_dense, pin_sddmm_integer_exact, pin_softmax_closed_forms, pin_softmax_dense,
+            pin_softmax_invariants, pin_aggregate_dense, pin_aggregate_integer_exact,
+            pin_zero_rows_positive_zero, pin_softmax_aggregate_dense, pin_softmax_aggregate_closed_forms,
+            pin_layer_dense]
+
+
+def run_all(orc) -> list:
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError as exc:  # a failing comparison
+            failed.append((pin.__name__, str(exc).splitlines()[0] if str(exc) else ""))
+    return failed
+
+
+if __name__ == "__main__":
+    import oracle as _oracle
+    lib = sys.argv[1] if len(sys.argv) > 1 else _oracle.LIB
+    fails = run_all(_oracle.Oracle(lib))
+    for name, msg in fails:
+        print("FAIL", name, msg)
+    sys.exit(min(len(fails), 100))

@@ -1,0 +1,66 @@
+"""The CPU oracle against its pins, and planted mistakes against the pins.
+
+The pins live in ``tests/oracle_pins.py``.  The mutation test copies
+``oracle/oracle.c``, plants one plausible mistake (a dropped term, a wrong
+index, a transposed operand, an off-by-one bound, a wrong sign), compiles it,
+runs every pin in a child process and requires at least one pin to fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build()
+    return oracle.Oracle()
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# (name, text in oracle.c, replacement); every mutant must stay in bounds.
+MUTANTS = [
+    ("softmax_no_max_shift", "double m = -INFINITY;", "double m = 0.0;"),
+    ("softmax_z_unshifted", "z += exp(scores[e * heads + h] - m);", "z += exp(scores[e * heads + h]);"),
+    ("softmax_not_normalised", "exp(scores[e * heads + h] - m) / z;", "exp(scores[e * heads + h] - m);"),
+    ("softmax_end_off_by_one", "for (int64_t e = start; e < end; ++e)\n                z +=",
+     "for (int64_t e = start; e + 1 < end; ++e)\n                z +="),
+    ("aggregate_head_dropped_in_gather", "((int64_t)col_idx[e] * heads + h) * head_dim + d",
+     "((int64_t)col_idx[e] * heads) * head_dim + d"),
+    ("aggregate_weight_head0", "acc += weights[e * heads + h] *", "acc += weights[e * heads] *"),
+    ("aggregate_end_off_by_one", "for (int64_t e = start; e < end; ++e)\n                    acc +=",
+     "for (int64_t e = start; e + 1 < end; ++e)\n                    acc +="),
+    ("aggregate_negative_zero_start", "double acc = 0.0;\n                for (int64_t e",
+     "double acc = -0.0;\n                for (int64_t e"),
+    ("sddmm_operands_swapped", "int64_t a = ((int64_t)dst_idx[e] * heads + h) * head_dim;",
+     "int64_t a = ((int64_t)src_idx[e] * heads + h) * head_dim;"),
+    ("sddmm_scale_dropped", "out[e * heads + h] = scale * acc;", "out[e * heads + h] = acc;"),
+    ("sddmm_dim_off_by_one", "for (int d = 0; d < head_dim; ++d)\n                acc +=",
+     "for (int d = 1; d < head_dim; ++d)\n                acc +="),
+    ("bf16_decode_shift", "<< 16;", "<< 15;"),
+    ("layer_query_row_wrong", "dst[e] = (int32_t)i;", "dst[e] = 0;"),
+    ("layer_k_v_swapped", "scores, v, dtype, out);", "scores, k, dtype, out);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_fails_a_pin(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = oracle.build(str(mut), str(tmp_path / "liboracle_mut.so"))
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), lib],
+                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode > 0, f"planted mistake {name} passed every pin:\n{r.stdout}{r.stderr}"
+    assert "Traceback" not in r.stderr, r.stderr
