@@ -1,0 +1,186 @@
+/*
+ * gat.h -- C-ABI of libgat.so: CSR graph-attention message passing on MI355X (gfx950).
+ *
+ * The operations follow the POPCORNBENCH kernel-writing transcripts:
+ *   [l1_p10] edge-only SDDMM, reference-model passage: out[e] is the dot product of
+ *            src_feat[src_idx[e]] and dst_feat[dst_idx[e]] over the feature dim.
+ *   [l1_p6]  multi-head row-wise softmax over CSR edge scores, reference-model
+ *            passage: for every node and head, softmax over the node's edge slice,
+ *            computed as exp(x - max) / sum(exp(x - max)).
+ *   [l1_p18] multi-head sparse aggregation with per-edge, per-head weights, task
+ *            statement: out[i,h,:] = sum over the row's edges of
+ *            edge_weight[e,h] * node_feat[col_idx[e],h,:], starting from zeros.
+ *   [l2_p37] CSR graph-attention neighbourhood softmax + aggregation, reference-model
+ *            passage: softmax over the row's edge scores, then the weighted sum of
+ *            node_value[col_idx[e]]; a row without edges keeps a zero output.
+ * The full layer (scores q_i . k_j computed on the fly, then [l2_p37] on v) is the
+ * composition of those steps.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers (memory of the current HIP device) unless the
+ *    comment says host.  The caller owns every buffer; the library allocates and
+ *    frees nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without waiting.  No entry point synchronises.
+ *  - Layouts (row-major, contiguous):
+ *      row_ptr  int32 [n_rows + 1], row_ptr[0] = 0, non-decreasing, row_ptr[n_rows] = n_edges
+ *      col_idx  int32 [n_edges], 0 <= col_idx[e] < n_src; edges of row i are
+ *               [row_ptr[i], row_ptr[i+1]); duplicates are allowed and each is its
+ *               own softmax term; order inside a row is free
+ *      scores / weights / alpha   fp32 [n_edges, heads] (edge-major)
+ *      features (feat, q, k, v, src_feat, dst_feat)  [n, heads, head_dim] of
+ *               dtype GAT_F32 (float) or GAT_BF16 (raw bfloat16 bits)
+ *      out of aggregate / fused_layer   fp32 [n_rows, heads, head_dim]
+ *    The CSR/COO preconditions above are not checked on the device.
+ *  - Supported shapes: head_dim in {16, 32, 64, 128}, heads in {1, 2, 4, 8, 16},
+ *    heads * head_dim <= 1024; anything else returns GAT_ERR_UNSUPPORTED.
+ *    n_rows and n_src must be in [0, 2^31 - 1], n_edges in [0, 2^31 - 4097]
+ *    (GAT_ERR_SIZE otherwise).
+ *  - Arithmetic is fp32 (bf16 inputs are widened exactly); exp is the hardware
+ *    exp2 of x*log2(e).  Outputs are fully overwritten: a row without edges gets
+ *    +0.0 in every element, so outputs need no clearing.
+ *  - Errors: every argument check runs on the host before anything is enqueued;
+ *    a failed check returns its status and enqueues nothing.  A launch failure
+ *    returns GAT_ERR_HIP.  No C++ exception crosses this interface.
+ */
+#ifndef GAT_H
+#define GAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gat_dtype { GAT_F32 = 0, GAT_BF16 = 1 } gat_dtype;
+
+typedef enum gat_status {
+    GAT_OK = 0,
+    GAT_ERR_NULL = 1,         /* a required pointer is NULL */
+    GAT_ERR_SIZE = 2,         /* a size is negative or does not fit int32 */
+    GAT_ERR_UNSUPPORTED = 3,  /* (heads, head_dim, dtype) outside the supported set */
+    GAT_ERR_WORKSPACE = 4,    /* plan workspace too small, or plan built for other sizes */
+    GAT_ERR_ARGS = 5,         /* inconsistent arguments (e.g. both or neither of scores / q,k) */
+    GAT_ERR_HIP = 6           /* a HIP call or kernel launch failed */
+} gat_status;
+
+/* Degree-binning defaults: rows with deg <= short_max are handled by one lane group
+ * (a wave or a fraction of one); rows with short_max < deg <= seg_len by one
+ * 256-thread workgroup; longer rows are split into segments of seg_len edges
+ * whose partial results are merged afterwards. */
+#define GAT_DEFAULT_SHORT_MAX 32
+#define GAT_DEFAULT_SEG_LEN 2048
+
+/*
+ * Degree-binning plan.  Host-side POD filled by gat_plan_build; the tables it
+ * points to live in the caller's device workspace `ws`.  A plan is valid for the
+ * row_ptr it was built from, while `ws` is alive and unchanged.  Fields are
+ * read-only for the caller (tests inspect the tables through the offsets).
+ *   segment table  int32 [seg_capacity][4]: (row, e_begin, e_end, slot); every
+ *                  hub segment first (slot = its index), then every long row
+ *                  (slot = -1), both in increasing row id.
+ *   hub table      int32 [hub_capacity][4]: (row, first segment, n segments, 0)
+ *   counts         int32 [8]: n_segments, n_hub_segments, n_hubs, n_long_rows
+ *   partials       fp32 [hubseg_capacity][state_floats]: per hub segment
+ *                  (max[heads], sum[heads], acc[heads*head_dim])
+ */
+typedef struct gat_plan {
+    int64_t n_rows, n_edges;
+    int32_t short_max, seg_len;
+    int32_t heads, head_dim;         /* partial-state capacity: calls need heads*(head_dim+2) <= state_floats */
+    int64_t state_floats;
+    int64_t seg_capacity, hub_capacity, hubseg_capacity;
+    int64_t n_blocks;                /* binner blocks */
+    void* ws;
+    size_t ws_bytes;
+    size_t off_counts, off_blocks, off_segs, off_hubs, off_partials;   /* byte offsets into ws */
+    uint32_t magic;
+} gat_plan;
+
+/*
+ * Bytes of device workspace gat_plan_build needs for these sizes.  heads/head_dim
+ * bound the partial-state size of later calls.  short_max < 0 or seg_len <= 0
+ * select the defaults.  Returns 0 for invalid sizes.  Host only; no HIP call.
+ */
+size_t gat_plan_workspace_bytes(int64_t n_rows, int64_t n_edges, int heads, int head_dim,
+                                int short_max, int seg_len);
+
+/*
+ * Degree binning (the plan): classifies every row by degree and writes the
+ * segment and hub tables into `ws` (device memory of at least
+ * gat_plan_workspace_bytes(...) bytes, 256-byte aligned).  Three kernels on
+ * `stream`; nothing is copied to the host, so the call does not synchronise --
+ * the kernels that use the plan read the counts on the device.  `plan` is a host
+ * pointer, filled before the call returns.
+ * This replaces the host-side maximum-degree pass of [l2_p37] (its passages on
+ * copying row_ptr to the host to size shared memory by max_degree).
+ */
+gat_status gat_plan_build(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges,
+                          int heads, int head_dim, int short_max, int seg_len,
+                          void* ws, size_t ws_bytes, gat_plan* plan, hipStream_t stream);
+
+/*
+ * SDDMM over an edge list [l1_p10], multi-head:
+ *   out[e,h] = scale * sum_d dst_feat[dst_idx[e],h,d] * src_feat[src_idx[e],h,d]
+ * src_idx/dst_idx int32 [n_edges]; src_feat [n_src,heads,head_dim]; dst_feat
+ * [n_dst,heads,head_dim]; out fp32 [n_edges,heads].  fp32 accumulation.
+ */
+gat_status gat_sddmm(const int32_t* src_idx, const int32_t* dst_idx, int64_t n_edges,
+                     const void* src_feat, int64_t n_src, const void* dst_feat, int64_t n_dst,
+                     gat_dtype dtype, int heads, int head_dim, float scale,
+                     float* out, hipStream_t stream);
+
+/*
+ * Row-wise multi-head edge softmax [l1_p6]:
+ *   alpha[e,h] = exp(s[e,h] - m_ih) / sum_{e' in row i} exp(s[e',h] - m_ih),  m_ih = max over the row
+ * scores/out fp32 [n_edges,heads]; out may equal scores (in place).  Entries of
+ * rows without edges do not exist.  plan: NULL (every row by one lane group) or a
+ * plan built for this row_ptr with heads*(head_dim+2) >= 2*heads.
+ */
+gat_status gat_edge_softmax(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, int heads,
+                            const float* scores, float* out, const gat_plan* plan, hipStream_t stream);
+
+/*
+ * Weighted aggregation / SpMM [l1_p18]:
+ *   out[i,h,:] = sum_{e in row i} weights[e,h] * feat[col_idx[e],h,:]   (+0.0 for rows without edges)
+ * weights fp32 [n_edges,heads]; feat [n_src,heads,head_dim] of `dtype`; out fp32
+ * [n_rows,heads,head_dim].  plan: NULL or built for this row_ptr.
+ */
+gat_status gat_aggregate(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                         int64_t n_edges, const float* weights, const void* feat, gat_dtype dtype,
+                         int heads, int head_dim, float* out, const gat_plan* plan, hipStream_t stream);
+
+/*
+ * Fused attention aggregation.  Exactly one of `scores` or the pair (q, k) must be
+ * non-NULL, else GAT_ERR_ARGS.
+ *  - scores given [l2_p37]: out = aggregate(edge_softmax(scores), v) in one pass;
+ *    the weights alpha never reach memory.
+ *  - q, k given (full layer): s[e,h] = scale * <q[i,h,:], k[col_idx[e],h,:]> is
+ *    computed on the fly (online max/sum), then the same aggregation of v; no
+ *    score reaches memory.  q [n_rows,heads,head_dim], k [n_src,heads,head_dim].
+ * v [n_src,heads,head_dim]; q/k/v share `dtype`; out fp32 [n_rows,heads,head_dim],
+ * +0.0 for rows without edges.  plan: NULL (every row by one lane group, correct
+ * for any degree) or a plan built for this row_ptr.
+ */
+gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                           int64_t n_edges, int heads, int head_dim, gat_dtype dtype,
+                           const float* scores, const void* q, const void* k, float scale,
+                           const void* v, float* out, const gat_plan* plan, hipStream_t stream);
+
+/* Static description of a status code (host; never NULL). */
+const char* gat_status_str(gat_status status);
+
+/* 1 if (heads, head_dim) is in the supported set, else 0 (host; no HIP call). */
+int gat_shape_supported(int heads, int head_dim);
+
+/* sizeof(gat_plan) as compiled into the library, for bindings that mirror the struct (host). */
+size_t gat_plan_sizeof(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GAT_H */

@@ -1,0 +1,116 @@
+// Device-side building blocks shared by the gfx950 kernels of libgat.
+//
+// Lane geometry.  A feature row of one node is H*D elements (H heads x D dims),
+// RB = H*D*sizeof(T) bytes.  It is read in 16-byte pieces (global_load_dwordx4):
+// NPC = RB/16 pieces.  A "slot" is the group of G = min(64, NPC) lanes that holds
+// one row; a wave64 holds P = 64/G slots, and each lane of a slot holds
+// NV = NPC/G pieces (piece index v*G + q for lane q of the slot).  A piece never
+// straddles two heads because D*sizeof(T) >= 32 bytes.
+//
+// Score layout.  A slot also reads edge scores [E,H] (edge-major) G values at a
+// time: lane q holds edge (chunk start + q/H), head q%H, so a chunk covers
+// SC = G/H edges and one coalesced dword load per lane fetches it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gat {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;            // threads per workgroup in every kernel
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+using bf16_t = uint16_t;                // raw bfloat16 bits
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> { static constexpr int bytes = 4; };
+template <>
+struct Elem<bf16_t> { static constexpr int bytes = 2; };
+
+template <typename T, int H_, int D_>
+struct Geo {
+    static constexpr int H = H_;
+    static constexpr int D = D_;
+    static constexpr int HD = H * D;
+    static constexpr int S = Elem<T>::bytes;
+    static constexpr int RB = HD * S;               // bytes per feature row
+    static constexpr int NPC = RB / 16;             // 16-byte pieces per row
+    static constexpr int G = NPC < kWave ? NPC : kWave;   // lanes per slot
+    static constexpr int P = kWave / G;             // slots per wave
+    static constexpr int NV = NPC / G;              // pieces per lane
+    static constexpr int EPP = 16 / S;              // elements per piece
+    static constexpr int LPH = D * S / 16;          // pieces per head
+    static constexpr int SC = G / H;                // edges per score chunk
+    static_assert(D * S >= 32, "a head must span at least two pieces");
+    static_assert(G % H == 0 && SC >= 1, "score chunk must hold whole edges");
+    static_assert(NPC % G == 0, "pieces must tile the lanes");
+};
+
+// ---------------------------------------------------------------------------- lane helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src); }
+__device__ __forceinline__ int shfl(int v, int src) { return __shfl(v, src); }
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask); }
+__device__ __forceinline__ int shfl_xor(int v, int mask) { return __shfl_xor(v, mask); }
+
+// e^x as the hardware exp2 of x*log2(e).  exp(-inf) = 0.
+__device__ __forceinline__ float exp_fast(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// ---------------------------------------------------------------------------- memory
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ void st16(void* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// widen one 16-byte piece to EPP floats (bf16 -> fp32 is exact: the bits move up 16 places)
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4& v, float* f);
+
+template <>
+__device__ __forceinline__ void unpack<float>(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+}
+
+template <>
+__device__ __forceinline__ void unpack<bf16_t>(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16);
+    f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16);
+    f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------------------- plan view
+// Device view of a degree-binning plan (see gat_plan in gat.h).
+struct PlanView {
+    const int32_t* counts;    // [0] n_segments [1] n_hub_segments [2] n_hubs [3] n_long
+    const int4* segs;         // (row, e_begin, e_end, slot)
+    const int4* hubs;         // (row, first segment, n segments, 0)
+    float* partials;          // [hub segment][state_floats]
+    int64_t state_floats;
+    int64_t seg_capacity;     // bounds on the table sizes (grid caps of the persistent kernels)
+    int64_t hub_capacity;
+    int64_t hubseg_capacity;
+    int32_t short_max;        // rows with deg <= short_max belong to the lane-group kernels
+    int32_t seg_len;
+};
+
+// Grid cap of the persistent kernels: 256 CUs x 8 workgroups.
+constexpr int64_t kPersistentBlocks = 2048;
+
+enum CountIdx { kNSegs = 0, kNHubSegs = 1, kNHubs = 2, kNLong = 3 };
+
+}  // namespace gat

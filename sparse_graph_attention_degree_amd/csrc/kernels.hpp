@@ -1,0 +1,99 @@
+// Host-side launch entry points of the gfx950 kernels (one per .hip file) and the
+// compile-time shape dispatch they share.  Everything here is internal to
+// libgat.so; the public interface is include/gat.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace gat {
+
+enum SpmmMode { kAgg = 0, kSoftAgg = 1, kLayer = 2 };
+
+// ---------------------------------------------------------------------------- dispatch
+template <typename T, int H_, int D_>
+struct ShapeTag {
+    using type = T;
+    static constexpr int H = H_;
+    static constexpr int D = D_;
+};
+
+template <int H, int D, typename F>
+bool dispatch_dtype(int dtype, F&& f) {
+    if constexpr (H * D <= 1024) {
+        if (dtype == 0) { f(ShapeTag<float, H, D>{}); return true; }
+        if (dtype == 1) { f(ShapeTag<bf16_t, H, D>{}); return true; }
+    }
+    return false;
+}
+
+template <int H, typename F>
+bool dispatch_dim(int dtype, int D, F&& f) {
+    switch (D) {
+        case 16: return dispatch_dtype<H, 16>(dtype, f);
+        case 32: return dispatch_dtype<H, 32>(dtype, f);
+        case 64: return dispatch_dtype<H, 64>(dtype, f);
+        case 128: return dispatch_dtype<H, 128>(dtype, f);
+        default: return false;
+    }
+}
+
+// Calls f(ShapeTag<T, H, D>{}) for a supported (dtype, H, D); returns false otherwise.
+template <typename F>
+bool dispatch_shape(int dtype, int H, int D, F&& f) {
+    switch (H) {
+        case 1: return dispatch_dim<1>(dtype, D, f);
+        case 2: return dispatch_dim<2>(dtype, D, f);
+        case 4: return dispatch_dim<4>(dtype, D, f);
+        case 8: return dispatch_dim<8>(dtype, D, f);
+        case 16: return dispatch_dim<16>(dtype, D, f);
+        default: return false;
+    }
+}
+
+template <typename F>
+bool dispatch_heads(int H, F&& f) {
+    switch (H) {
+        case 1: f(ShapeTag<float, 1, 0>{}); return true;
+        case 2: f(ShapeTag<float, 2, 0>{}); return true;
+        case 4: f(ShapeTag<float, 4, 0>{}); return true;
+        case 8: f(ShapeTag<float, 8, 0>{}); return true;
+        case 16: f(ShapeTag<float, 16, 0>{}); return true;
+        default: return false;
+    }
+}
+
+inline unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
+    int64_t g = (items + per_block - 1) / per_block;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+// ---------------------------------------------------------------------------- launchers
+// Every launcher enqueues on `stream` and returns hipGetLastError() (hipErrorInvalidValue
+// for an unsupported shape, which the C-ABI has already ruled out).
+
+hipError_t launch_plan(const int32_t* row_ptr, int64_t n_rows, int short_max, int seg_len,
+                       int4* blocks, int64_t n_blocks, int32_t* counts, int4* segs, int4* hubs,
+                       hipStream_t stream);
+
+hipError_t launch_sddmm(int dtype, int H, int D, const int32_t* src_idx, const int32_t* dst_idx,
+                        int64_t n_edges, const void* src_feat, const void* dst_feat, float scale,
+                        float* out, hipStream_t stream);
+
+hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const float* scores,
+                          float* out, const PlanView* plan, hipStream_t stream);
+
+// mode kAgg: weights in `scores`; kSoftAgg: scores; kLayer: q, k (scores unused).
+hipError_t launch_spmm(int mode, int dtype, int H, int D, const int32_t* row_ptr, const int32_t* col_idx,
+                       int64_t n_rows, const float* scores, const void* q, const void* k, const void* v,
+                       float scale, float* out, const PlanView* plan, hipStream_t stream);
+
+// Rows per binner block (256 threads x 4 consecutive rows).
+constexpr int kPlanRowsPerThread = 4;
+constexpr int kPlanRowsPerBlock = kBlock * kPlanRowsPerThread;
+
+}  // namespace gat

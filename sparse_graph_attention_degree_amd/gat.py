@@ -1,0 +1,237 @@
+"""ctypes binding of libgat.so (include/gat.h).  Argument marshalling only.
+
+Every function takes torch tensors that already live on the current HIP device,
+checks dtype / shape / contiguity, and calls the C entry point of the same name
+with raw device pointers and the current torch stream.  Every step of the path
+runs in the library's gfx950 kernels; there is no CPU fallback -- a missing
+library or a CPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgat.so")
+
+GAT_F32, GAT_BF16 = 0, 1
+STATUS = {0: "GAT_OK", 1: "GAT_ERR_NULL", 2: "GAT_ERR_SIZE", 3: "GAT_ERR_UNSUPPORTED", 4: "GAT_ERR_WORKSPACE",
+          5: "GAT_ERR_ARGS", 6: "GAT_ERR_HIP"}
+DEFAULT_SHORT_MAX = 32
+DEFAULT_SEG_LEN = 2048
+
+EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge_softmax", "gat_aggregate",
+            "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof"]
+
+
+class GatError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({_lib().gat_status_str(status).decode()})")
+
+
+class GatPlanStruct(ctypes.Structure):
+    """Mirror of ``gat_plan`` (checked against gat_plan_sizeof at load)."""
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_edges", ctypes.c_int64),
+                ("short_max", ctypes.c_int32), ("seg_len", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("state_floats", ctypes.c_int64),
+                ("seg_capacity", ctypes.c_int64), ("hub_capacity", ctypes.c_int64),
+                ("hubseg_capacity", ctypes.c_int64), ("n_blocks", ctypes.c_int64),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("off_counts", ctypes.c_size_t), ("off_blocks", ctypes.c_size_t), ("off_segs", ctypes.c_size_t),
+                ("off_hubs", ctypes.c_size_t), ("off_partials", ctypes.c_size_t),
+                ("magic", ctypes.c_uint32)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    L.gat_plan_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    L.gat_plan_workspace_bytes.restype = sz
+    L.gat_plan_build.argtypes = [vp, i64, i64, i32, i32, i32, i32, vp, sz, ctypes.POINTER(GatPlanStruct), vp]
+    L.gat_sddmm.argtypes = [vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, f32, vp, vp]
+    L.gat_edge_softmax.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    L.gat_aggregate.argtypes = [vp, vp, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.gat_fused_layer.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, vp]
+    for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer):
+        f.restype = i32
+    L.gat_status_str.argtypes = [i32]
+    L.gat_status_str.restype = ctypes.c_char_p
+    L.gat_shape_supported.argtypes = [i32, i32]
+    L.gat_shape_supported.restype = i32
+    L.gat_plan_sizeof.restype = sz
+    if L.gat_plan_sizeof() != ctypes.sizeof(GatPlanStruct):
+        raise RuntimeError("gat_plan layout mismatch between libgat.so and the binding")
+    _LIB = L
+    return L
+
+
+def lib():
+    """The loaded ctypes library (raises if not built)."""
+    return _lib()
+
+
+# ----------------------------------------------------------------------------- marshalling
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise GatError(fn, status)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (libgat has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _feat_dtype(t):
+    if t.dtype == torch.float32:
+        return GAT_F32
+    if t.dtype == torch.bfloat16:
+        return GAT_BF16
+    raise TypeError(f"features must be float32 or bfloat16, got {t.dtype}")
+
+
+# ----------------------------------------------------------------------------- plan
+class Plan:
+    """A degree-binning plan plus the device workspace that holds its tables."""
+
+    def __init__(self, struct: GatPlanStruct, ws: torch.Tensor):
+        self.struct = struct
+        self.ws = ws
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+    def table(self, which: str) -> torch.Tensor:
+        """View of a plan table in the workspace (int32), for inspection."""
+        s = self.struct
+        if which == "counts":
+            off, n = s.off_counts, 8
+        elif which == "segs":
+            off, n = s.off_segs, 4 * s.seg_capacity
+        elif which == "hubs":
+            off, n = s.off_hubs, 4 * s.hub_capacity
+        else:
+            raise KeyError(which)
+        return self.ws[off:off + 4 * n].view(torch.int32)
+
+
+def gat_plan_workspace_bytes(n_rows, n_edges, heads, head_dim, short_max=-1, seg_len=0) -> int:
+    return int(_lib().gat_plan_workspace_bytes(n_rows, n_edges, heads, head_dim, short_max, seg_len))
+
+
+def gat_plan_build(row_ptr: torch.Tensor, n_edges: int, heads: int, head_dim: int, short_max: int = -1,
+                   seg_len: int = 0, ws: torch.Tensor | None = None, stream=None) -> Plan:
+    """Build a degree-binning plan on the device (no synchronisation).  Allocates the
+    workspace with torch unless ``ws`` (uint8, 256-byte aligned) is given."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    n_rows = row_ptr.numel() - 1
+    need = gat_plan_workspace_bytes(n_rows, n_edges, heads, head_dim, short_max, seg_len)
+    if need == 0:
+        raise GatError("gat_plan_workspace_bytes", 2)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=row_ptr.device)
+    _dev(ws, "ws", torch.uint8, 1)
+    st = GatPlanStruct()
+    _check("gat_plan_build", _lib().gat_plan_build(_ptr(row_ptr), n_rows, n_edges, heads, head_dim, short_max,
+                                                   seg_len, _ptr(ws), ws.numel(), ctypes.byref(st),
+                                                   _stream(stream)))
+    return Plan(st, ws)
+
+
+# ----------------------------------------------------------------------------- operations
+def gat_sddmm(src_idx, dst_idx, src_feat, dst_feat, scale: float = 1.0, out=None, stream=None):
+    """out[e,h] = scale * <dst_feat[dst_idx[e],h,:], src_feat[src_idx[e],h,:]>; returns fp32 [E,H]."""
+    _dev(src_idx, "src_idx", torch.int32, 1)
+    _dev(dst_idx, "dst_idx", torch.int32, 1)
+    _dev(src_feat, "src_feat", None, 3)
+    _dev(dst_feat, "dst_feat", src_feat.dtype, 3)
+    E = src_idx.numel()
+    if dst_idx.numel() != E or dst_feat.shape[1:] != src_feat.shape[1:]:
+        raise ValueError("inconsistent sddmm shapes")
+    H, D = src_feat.shape[1:]
+    if out is None:
+        out = torch.empty((E, H), dtype=torch.float32, device=src_feat.device)
+    _dev(out, "out", torch.float32, 2)
+    _check("gat_sddmm", _lib().gat_sddmm(_ptr(src_idx), _ptr(dst_idx), E, _ptr(src_feat), src_feat.shape[0],
+                                         _ptr(dst_feat), dst_feat.shape[0], _feat_dtype(src_feat), H, D,
+                                         float(scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def gat_edge_softmax(row_ptr, scores, out=None, plan: Plan | None = None, stream=None):
+    """Row-wise multi-head softmax of fp32 scores [E,H]; ``out`` may be ``scores``."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(scores, "scores", torch.float32, 2)
+    E, H = scores.shape
+    if out is None:
+        out = torch.empty_like(scores)
+    _dev(out, "out", torch.float32, 2)
+    _check("gat_edge_softmax", _lib().gat_edge_softmax(_ptr(row_ptr), row_ptr.numel() - 1, E, H, _ptr(scores),
+                                                       _ptr(out), plan.ref() if plan else None, _stream(stream)))
+    return out
+
+
+def gat_aggregate(row_ptr, col_idx, weights, feat, out=None, plan: Plan | None = None, stream=None):
+    """out[i,h,:] = sum_e weights[e,h] * feat[col_idx[e],h,:]; returns fp32 [N,H,D]."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(col_idx, "col_idx", torch.int32, 1)
+    _dev(weights, "weights", torch.float32, 2)
+    _dev(feat, "feat", None, 3)
+    n_rows = row_ptr.numel() - 1
+    H, D = feat.shape[1:]
+    if out is None:
+        out = torch.empty((n_rows, H, D), dtype=torch.float32, device=feat.device)
+    _dev(out, "out", torch.float32, 3)
+    _check("gat_aggregate", _lib().gat_aggregate(_ptr(row_ptr), _ptr(col_idx), n_rows, feat.shape[0],
+                                                 col_idx.numel(), _ptr(weights), _ptr(feat), _feat_dtype(feat), H,
+                                                 D, _ptr(out), plan.ref() if plan else None, _stream(stream)))
+    return out
+
+
+def gat_fused_layer(row_ptr, col_idx, v, scores=None, q=None, k=None, scale: float = 1.0, out=None,
+                    plan: Plan | None = None, stream=None):
+    """Fused softmax + aggregation of v with given scores, or with scores q_i . k_j computed on the fly."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(col_idx, "col_idx", torch.int32, 1)
+    _dev(v, "v", None, 3)
+    _dev(scores, "scores", torch.float32, 2)
+    _dev(q, "q", v.dtype, 3)
+    _dev(k, "k", v.dtype, 3)
+    n_rows = row_ptr.numel() - 1
+    H, D = v.shape[1:]
+    if out is None:
+        out = torch.empty((n_rows, H, D), dtype=torch.float32, device=v.device)
+    _dev(out, "out", torch.float32, 3)
+    _check("gat_fused_layer", _lib().gat_fused_layer(_ptr(row_ptr), _ptr(col_idx), n_rows, v.shape[0],
+                                                     col_idx.numel(), H, D, _feat_dtype(v), _ptr(scores), _ptr(q),
+                                                     _ptr(k), float(scale), _ptr(v), _ptr(out),
+                                                     plan.ref() if plan else None, _stream(stream)))
+    return out

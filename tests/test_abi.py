@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/gat.h declares, the ctypes mirror of gat_plan matches, and every
+host-side argument check returns its status before anything touches the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from sparse_graph_attention_degree_amd import gat
+from sparse_graph_attention_degree_amd import graphs as G
+import oracle.binning as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gat.h")
+
+OK, NULL, SIZE, UNSUP, WS, ARGS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gat.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return gat.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gat_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for op in ("gat_sddmm", "gat_edge_softmax", "gat_aggregate", "gat_fused_layer", "gat_plan_build"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    nm = subprocess.run(["nm", "-D", "--defined-only", gat.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (gat_\w+)$", nm.stdout, flags=re.M))
+    declared = set(declared_functions())
+    assert declared <= exported, f"missing exports: {declared - exported}"
+    assert set(gat.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_plan_struct_layout(L):
+    assert L.gat_plan_sizeof() == ctypes.sizeof(gat.GatPlanStruct)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.gat_status_str(s)
+    assert L.gat_status_str(99) == b"unknown status"
+
+
+def test_supported_shapes(L):
+    ok = [(h, d) for h in (1, 2, 4, 8, 16) for d in (16, 32, 64, 128) if h * d <= 1024]
+    for h in range(0, 20):
+        for d in (0, 8, 16, 24, 32, 64, 128, 256):
+            assert L.gat_shape_supported(h, d) == int((h, d) in ok)
+
+
+def test_workspace_bytes(L):
+    assert L.gat_plan_workspace_bytes(-1, 10, 4, 64, -1, 0) == 0
+    assert L.gat_plan_workspace_bytes(10, 2**31, 4, 64, -1, 0) == 0
+    assert L.gat_plan_workspace_bytes(10, 10, 3, 64, -1, 0) == 0
+    a = L.gat_plan_workspace_bytes(2**20, 2**24, 4, 64, -1, 0)
+    b = L.gat_plan_workspace_bytes(2**20, 2**24, 4, 64, 0, 1)
+    assert 0 < a < b and a % 256 == 0
+    assert L.gat_plan_workspace_bytes(0, 0, 1, 16, -1, 0) > 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails a host check first
+
+
+def test_sddmm_host_checks(L):
+    f = L.gat_sddmm
+    assert f(FAKE, FAKE, -1, FAKE, 4, FAKE, 4, 0, 1, 64, 1.0, FAKE, None) == SIZE
+    assert f(FAKE, FAKE, 10, FAKE, 2**31, FAKE, 4, 0, 1, 64, 1.0, FAKE, None) == SIZE
+    assert f(FAKE, FAKE, 10, FAKE, 4, FAKE, 4, 0, 3, 64, 1.0, FAKE, None) == UNSUP
+    assert f(FAKE, FAKE, 10, FAKE, 4, FAKE, 4, 0, 16, 128, 1.0, FAKE, None) == UNSUP
+    assert f(FAKE, FAKE, 10, FAKE, 4, FAKE, 4, 7, 1, 64, 1.0, FAKE, None) == UNSUP
+    assert f(None, FAKE, 10, FAKE, 4, FAKE, 4, 0, 1, 64, 1.0, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 10, FAKE, 4, FAKE, 4, 0, 1, 64, 1.0, None, None) == NULL
+    assert f(FAKE, FAKE, 10, FAKE, 0, FAKE, 4, 0, 1, 64, 1.0, FAKE, None) == ARGS
+    assert f(None, None, 0, None, 0, None, 0, 0, 1, 64, 1.0, None, None) == OK   # nothing to do
+
+
+def test_softmax_host_checks(L):
+    f = L.gat_edge_softmax
+    assert f(FAKE, -1, 5, 1, FAKE, FAKE, None, None) == SIZE
+    assert f(FAKE, 4, 5, 3, FAKE, FAKE, None, None) == UNSUP
+    assert f(None, 4, 5, 1, FAKE, FAKE, None, None) == NULL
+    assert f(FAKE, 4, 5, 1, None, FAKE, None, None) == NULL
+    assert f(None, 0, 0, 1, None, None, None, None) == OK
+    bad = gat.GatPlanStruct()   # magic not set
+    assert f(FAKE, 4, 5, 1, FAKE, FAKE, ctypes.byref(bad), None) == ARGS
+
+
+def test_aggregate_host_checks(L):
+    f = L.gat_aggregate
+    assert f(FAKE, FAKE, 4, 4, -2, FAKE, FAKE, 0, 1, 64, FAKE, None, None) == SIZE
+    assert f(FAKE, FAKE, 4, 4, 5, FAKE, FAKE, 0, 1, 48, FAKE, None, None) == UNSUP
+    assert f(FAKE, FAKE, 4, 4, 5, FAKE, FAKE, 2, 1, 64, FAKE, None, None) == UNSUP
+    assert f(None, FAKE, 4, 4, 5, FAKE, FAKE, 0, 1, 64, FAKE, None, None) == NULL
+    assert f(FAKE, FAKE, 4, 4, 5, None, FAKE, 0, 1, 64, FAKE, None, None) == NULL
+    assert f(FAKE, FAKE, 4, 0, 5, FAKE, FAKE, 0, 1, 64, FAKE, None, None) == ARGS
+    assert f(None, None, 0, 0, 0, None, None, 0, 1, 64, None, None, None) == OK
+
+
+def test_fused_layer_host_checks(L):
+    f = L.gat_fused_layer
+    args = lambda sc, q, k: (FAKE, FAKE, 4, 4, 5, 4, 64, 0, sc, q, k, 1.0, FAKE, FAKE, None, None)  # noqa: E731
+    assert f(*args(FAKE, FAKE, FAKE)) == ARGS      # both scores and q,k
+    assert f(*args(None, None, None)) == ARGS      # neither
+    assert f(*args(None, FAKE, None)) == ARGS      # q without k
+    assert f(*args(None, None, FAKE)) == ARGS      # k without q
+    assert f(FAKE, FAKE, 4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, None, FAKE, None, None) == NULL   # v missing
+    assert f(FAKE, FAKE, 4, 4, 5, 5, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None, None) == UNSUP
+    assert f(FAKE, FAKE, -4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None, None) == SIZE
+
+
+def test_plan_build_host_checks(L):
+    f = L.gat_plan_build
+    p = gat.GatPlanStruct()
+    need = L.gat_plan_workspace_bytes(100, 1000, 4, 64, -1, 0)
+    assert f(FAKE, 100, 1000, 4, 64, -1, 0, FAKE, need, None, None) == NULL
+    assert f(None, 100, 1000, 4, 64, -1, 0, FAKE, need, ctypes.byref(p), None) == NULL
+    assert f(FAKE, 100, 1000, 4, 64, -1, 0, ctypes.c_void_p(0x1010), need, ctypes.byref(p), None) == ARGS
+    assert f(FAKE, 100, 1000, 4, 64, -1, 0, FAKE, need - 1, ctypes.byref(p), None) == WS
+    assert f(FAKE, 100, 1000, 5, 64, -1, 0, FAKE, need, ctypes.byref(p), None) == UNSUP
+    assert f(FAKE, -100, 1000, 4, 64, -1, 0, FAKE, need, ctypes.byref(p), None) == SIZE
+
+
+def test_binning_reference_tiles_rows():
+    """The CPU binning statement: classes partition the rows; hub segments tile each hub row once."""
+    r = np.random.default_rng(0)
+    deg = np.concatenate([r.integers(0, 40, 500), [5000, 2049, 2048, 33, 32, 0, 12000]])
+    rp = G.row_ptr_from_degrees(deg)
+    for short_max, seg_len in [(32, 2048), (0, 1), (0, 7), (100, 64), (2**31 - 1, 2048)]:
+        segs, hubs, nhs = B.plan(rp, short_max, seg_len)
+        cls = B.classify(rp, short_max, seg_len)
+        covered = np.zeros(rp[-1], np.int32)
+        for row, b, e, slot in segs:
+            assert rp[row] <= b < e <= rp[row + 1] and e - b <= max(seg_len, short_max + 1, 1) + seg_len
+            covered[b:e] += 1
+        nonshort = np.flatnonzero(cls > 0)
+        for i in nonshort:
+            assert np.all(covered[rp[i]:rp[i + 1]] == 1)
+        assert covered.sum() == sum(deg[i] for i in nonshort)
+        assert nhs == sum(-(-deg[i] // seg_len) for i in np.flatnonzero(cls == 2))
+        assert np.all(segs[:nhs, 3] == np.arange(nhs)) and np.all(segs[nhs:, 3] == -1)
