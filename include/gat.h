@@ -154,8 +154,9 @@ gat_status gat_aggregate(const int32_t* row_ptr, const int32_t* col_idx, int64_t
                          int heads, int head_dim, float* out, const gat_plan* plan, hipStream_t stream);
 
 /*
- * Fused attention aggregation.  Exactly one of `scores` or the pair (q, k) must be
- * non-NULL, else GAT_ERR_ARGS.
+ * Fused attention aggregation.  When n_edges > 0, exactly one of `scores` or the
+ * pair (q, k) must be non-NULL, else GAT_ERR_ARGS (with no edges every output row
+ * is +0.0 and the pointers are not read).
  *  - scores given [l2_p37]: out = aggregate(edge_softmax(scores), v) in one pass;
  *    the weights alpha never reach memory.
  *  - q, k given (full layer): s[e,h] = scale * <q[i,h,:], k[col_idx[e],h,:]> is

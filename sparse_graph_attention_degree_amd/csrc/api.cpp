@@ -248,7 +248,8 @@ gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64
     if (!shape_ok(heads, head_dim) || !dtype_ok(dtype)) return GAT_ERR_UNSUPPORTED;
     const bool have_scores = scores != nullptr;
     const bool have_q = q != nullptr, have_k = k != nullptr;
-    if (have_q != have_k || have_scores == have_q) return GAT_ERR_ARGS;
+    // With no edges the output is +0.0 whatever the mode, and empty tensors carry NULL data pointers.
+    if (n_edges > 0 && (have_q != have_k || have_scores == have_q)) return GAT_ERR_ARGS;
     if (n_rows == 0) return GAT_OK;
     if (!row_ptr || !out) return GAT_ERR_NULL;
     if (n_edges > 0 && (!col_idx || !v)) return GAT_ERR_NULL;
