@@ -210,11 +210,21 @@ def main():
              "kernel_source_sha256": kernel_source_digest()}
 
     if not args.no_extra:
+        # the other rows of the path, each timed alone over the same graph (5 calls, HIP events)
         plan = gat.gat_plan_build(rp, E, H, D, ws=ws)
-        for name, fn in [
-            ("full_layer_qk_on_the_fly", lambda: gat.gat_fused_layer(rp, col, vd, q=qd, k=kd, out=out, plan=plan)),
-            ("fused_no_plan", lambda: gat.gat_fused_layer(rp, col, vd, scores=scores, out=out)),
-        ]:
+        alpha = torch.empty_like(scores)
+        gat.gat_edge_softmax(rp, scores, out=alpha, plan=plan)
+        row_bytes = {
+            "edge_softmax": (4 * (N + 1) + 8 * E * H,
+                             lambda: gat.gat_edge_softmax(rp, scores, out=alpha, plan=plan)),
+            "aggregate": (fused_alg_bytes(N, E, H, D, feat_bytes),
+                          lambda: gat.gat_aggregate(rp, col, alpha, vd, out=out, plan=plan)),
+            "full_layer_qk_on_the_fly": (4 * (N + 1) + 4 * E + N * H * D * feat_bytes
+                                         + 2 * E * H * D * feat_bytes + 4 * N * H * D,
+                                         lambda: gat.gat_fused_layer(rp, col, vd, q=qd, k=kd, out=out, plan=plan)),
+            "fused_no_plan": (alg, lambda: gat.gat_fused_layer(rp, col, vd, scores=scores, out=out)),
+        }
+        for name, (nbytes, fn) in row_bytes.items():
             fn()
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -227,6 +237,8 @@ def main():
             t = s0.elapsed_time(s1) * 1e-3 / reps
             extra[f"{name}_ms"] = t * 1e3
             extra[f"{name}_edge_heads_per_s"] = E * H / t
+            extra[f"{name}_alg_bytes"] = nbytes
+            extra[f"{name}_gbs"] = nbytes / t / 1e9
 
     cpu = None
     if not args.no_cpu:

@@ -71,8 +71,8 @@ typedef enum gat_status {
  * (a wave or a fraction of one); rows with short_max < deg <= seg_len by one
  * 256-thread workgroup; longer rows are split into segments of seg_len edges
  * whose partial results are merged afterwards. */
-#define GAT_DEFAULT_SHORT_MAX 32
-#define GAT_DEFAULT_SEG_LEN 2048
+#define GAT_DEFAULT_SHORT_MAX 64
+#define GAT_DEFAULT_SEG_LEN 1024
 
 /*
  * Degree-binning plan.  Host-side POD filled by gat_plan_build; the tables it

@@ -9,24 +9,24 @@
 #include "kernels.hpp"
 
 namespace gat {
-hipError_t launch_spmm_agg(int, int, int, const int32_t*, const int32_t*, int64_t, const float*, const void*,
-                           const void*, const void*, float, float*, const PlanView*, hipStream_t);
-hipError_t launch_spmm_softagg(int, int, int, const int32_t*, const int32_t*, int64_t, const float*, const void*,
-                               const void*, const void*, float, float*, const PlanView*, hipStream_t);
-hipError_t launch_spmm_layer(int, int, int, const int32_t*, const int32_t*, int64_t, const float*, const void*,
-                             const void*, const void*, float, float*, const PlanView*, hipStream_t);
+hipError_t launch_spmm_agg(int, int, int, const int32_t*, const int32_t*, int64_t, int64_t, const float*,
+                           const void*, const void*, const void*, float, float*, const PlanView*, hipStream_t);
+hipError_t launch_spmm_softagg(int, int, int, const int32_t*, const int32_t*, int64_t, int64_t, const float*,
+                               const void*, const void*, const void*, float, float*, const PlanView*, hipStream_t);
+hipError_t launch_spmm_layer(int, int, int, const int32_t*, const int32_t*, int64_t, int64_t, const float*,
+                             const void*, const void*, const void*, float, float*, const PlanView*, hipStream_t);
 
 hipError_t launch_spmm(int mode, int dtype, int H, int D, const int32_t* row_ptr, const int32_t* col_idx,
-                       int64_t n_rows, const float* scores, const void* q, const void* k, const void* v, float scale,
+                       int64_t n_rows, int64_t n_src, const float* scores, const void* q, const void* k, const void* v, float scale,
                        float* out, const PlanView* plan, hipStream_t stream) {
     switch (mode) {
         case kAgg:
-            return launch_spmm_agg(dtype, H, D, row_ptr, col_idx, n_rows, scores, q, k, v, scale, out, plan, stream);
+            return launch_spmm_agg(dtype, H, D, row_ptr, col_idx, n_rows, n_src, scores, q, k, v, scale, out, plan, stream);
         case kSoftAgg:
-            return launch_spmm_softagg(dtype, H, D, row_ptr, col_idx, n_rows, scores, q, k, v, scale, out, plan,
+            return launch_spmm_softagg(dtype, H, D, row_ptr, col_idx, n_rows, n_src, scores, q, k, v, scale, out, plan,
                                        stream);
         case kLayer:
-            return launch_spmm_layer(dtype, H, D, row_ptr, col_idx, n_rows, scores, q, k, v, scale, out, plan,
+            return launch_spmm_layer(dtype, H, D, row_ptr, col_idx, n_rows, n_src, scores, q, k, v, scale, out, plan,
                                      stream);
         default:
             return hipErrorInvalidValue;
@@ -202,8 +202,8 @@ gat_status gat_sddmm(const int32_t* src_idx, const int32_t* dst_idx, int64_t n_e
     if (n_edges == 0) return GAT_OK;
     if (!src_idx || !dst_idx || !src_feat || !dst_feat || !out) return GAT_ERR_NULL;
     if (n_src == 0 || n_dst == 0) return GAT_ERR_ARGS;   // an edge needs a source and a destination row
-    return hip_status(gat::launch_sddmm(dtype, heads, head_dim, src_idx, dst_idx, n_edges, src_feat, dst_feat,
-                                        scale, out, stream));
+    return hip_status(gat::launch_sddmm(dtype, heads, head_dim, src_idx, dst_idx, n_edges, src_feat, n_src,
+                                        dst_feat, n_dst, scale, out, stream));
 }
 
 gat_status gat_edge_softmax(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, int heads,
@@ -236,7 +236,7 @@ gat_status gat_aggregate(const int32_t* row_ptr, const int32_t* col_idx, int64_t
         if (st != GAT_OK) return st;
         pv = plan_view(plan);
     }
-    return hip_status(gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, row_ptr, col_idx, n_rows, weights,
+    return hip_status(gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, weights,
                                        nullptr, nullptr, feat, 1.f, out, plan ? &pv : nullptr, stream));
 }
 
@@ -261,7 +261,7 @@ gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64
         pv = plan_view(plan);
     }
     const int mode = have_scores ? gat::kSoftAgg : gat::kLayer;
-    return hip_status(gat::launch_spmm(mode, dtype, heads, head_dim, row_ptr, col_idx, n_rows, scores, q, k, v,
+    return hip_status(gat::launch_spmm(mode, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, scores, q, k, v,
                                        scale, out, plan ? &pv : nullptr, stream));
 }
 

@@ -93,6 +93,36 @@ __device__ __forceinline__ void unpack<bf16_t>(const uint4& v, float* f) {
     f[7] = __uint_as_float(v.w & 0xffff0000u);
 }
 
+// ---------------------------------------------------------------------------- gathered tables
+// A feature table of rows of RB bytes, read 16 bytes at a time.
+//  Tab32: the table spans < 4 GiB.  Rows are read with buffer loads: the descriptor (base,
+//         size) sits in scalar registers and each lane supplies one 32-bit byte offset, so a
+//         gather costs one address instruction; an offset past the end reads 0.  The
+//         descriptor's fourth dword (0x00020000) is the gfx9-family raw-buffer format.
+//  Tab64: any size; 64-bit addresses.
+typedef int gat_v4i __attribute__((ext_vector_type(4)));
+
+template <int RB>
+struct Tab32 {
+    __amdgpu_buffer_rsrc_t rs;
+    __device__ __forceinline__ Tab32(const void* base, int64_t n_rows)
+        : rs(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)(n_rows * RB),
+                                                0x00020000)) {}
+    __device__ __forceinline__ uint4 row16(int r, uint32_t byte_off) const {
+        const gat_v4i x = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)r * (uint32_t)RB + byte_off, 0, 0);
+        return make_uint4((uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w);
+    }
+};
+
+template <int RB>
+struct Tab64 {
+    const char* base;
+    __device__ __forceinline__ Tab64(const void* b, int64_t) : base(static_cast<const char*>(b)) {}
+    __device__ __forceinline__ uint4 row16(int r, uint32_t byte_off) const {
+        return ld16(base + (int64_t)r * RB + byte_off);
+    }
+};
+
 // ---------------------------------------------------------------------------- plan view
 // Device view of a degree-binning plan (see gat_plan in gat.h).
 struct PlanView {

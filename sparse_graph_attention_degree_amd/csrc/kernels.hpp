@@ -53,6 +53,11 @@ bool dispatch_shape(int dtype, int H, int D, F&& f) {
     }
 }
 
+template <class T>
+struct TypeTag {
+    using type = T;
+};
+
 template <typename F>
 bool dispatch_heads(int H, F&& f) {
     switch (H) {
@@ -81,15 +86,15 @@ hipError_t launch_plan(const int32_t* row_ptr, int64_t n_rows, int short_max, in
                        hipStream_t stream);
 
 hipError_t launch_sddmm(int dtype, int H, int D, const int32_t* src_idx, const int32_t* dst_idx,
-                        int64_t n_edges, const void* src_feat, const void* dst_feat, float scale,
-                        float* out, hipStream_t stream);
+                        int64_t n_edges, const void* src_feat, int64_t n_src, const void* dst_feat,
+                        int64_t n_dst, float scale, float* out, hipStream_t stream);
 
 hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const float* scores,
                           float* out, const PlanView* plan, hipStream_t stream);
 
 // mode kAgg: weights in `scores`; kSoftAgg: scores; kLayer: q, k (scores unused).
 hipError_t launch_spmm(int mode, int dtype, int H, int D, const int32_t* row_ptr, const int32_t* col_idx,
-                       int64_t n_rows, const float* scores, const void* q, const void* k, const void* v,
+                       int64_t n_rows, int64_t n_src, const float* scores, const void* q, const void* k, const void* v,
                        float scale, float* out, const PlanView* plan, hipStream_t stream);
 
 // Rows per binner block (256 threads x 4 consecutive rows).

@@ -6,7 +6,11 @@
 // over the 128 features and a shuffle tree.  Here a slot of G lanes (common.hpp)
 // owns one edge and each lane takes 16-byte pieces of both rows, so one wave64
 // holds P edges per step and U steps of gathers are issued before any is used.
-// The per-head sum is an xor-shuffle tree over the LPH lanes of a head.
+// The per-head sum is an xor-shuffle tree over the LPH lanes of a head.  The waves
+// sweep the edge list together (grid-stride), so with edges sorted by destination
+// neighbouring waves share destination rows and output lines in L2; keeping the
+// destination row in registers across repeated destinations, prefetching the next
+// indices, and buffer loads each measured slower here and are not used.
 #include "kernels.hpp"
 
 namespace gat {
@@ -78,7 +82,8 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_sddmm(int dtype, int H, int D, const int32_t* src_idx, const int32_t* dst_idx, int64_t n_edges,
-                        const void* src_feat, const void* dst_feat, float scale, float* out, hipStream_t stream) {
+                        const void* src_feat, int64_t /*n_src*/, const void* dst_feat, int64_t /*n_dst*/,
+                        float scale, float* out, hipStream_t stream) {
     if (n_edges == 0) return hipSuccess;
     const bool ok = dispatch_shape(dtype, H, D, [&](auto tag) {
         using Tag = decltype(tag);

@@ -4,18 +4,24 @@
 //   kLayer   as kSoftAgg with s[e,h] = scale <q[i,h,:], k[col[e],h,:]> computed on the fly
 //
 // A slot (G lanes, see common.hpp) walks a stream of chunks: SC consecutive edges of one
-// row at a time.  A chunk's column ids (lanes q < SC) and scores (one dword per lane)
-// arrive with two coalesced loads; the source rows are gathered U edges at a time, all U
-// gathers issued before the first is used.  Right after a chunk's gathers are issued the
-// slot issues the loads of its NEXT chunk (the next edges of the row, or the first edges
-// of its next row), so the index/score round trip hides behind the gathers.
+// row at a time.  A chunk's column ids and scores (one dword per lane) arrive with two
+// coalesced loads; the source rows are gathered U edges at a time, all U gathers issued
+// before the first is used.  Before a chunk's gathers are issued the slot issues the loads
+// of its NEXT chunk (the next edges of the row, or the first edges of its next row; in
+// kLayer also that row's query), so their round trip hides behind the gathers and the
+// wait for the gathers never waits on a load issued after them.
 //
 // Softmax is kept online per row and head: a chunk's maximum c (xor-shuffle tree over
 // the lanes of one head) raises the running maximum m to m' = max(m, c); the running sum
 // and the accumulators are rescaled by e^(m-m') (skipped when no lane's maximum moved),
-// and each edge-head weight p = e^(s-m') is computed once, by the lane that loaded s,
-// then moved to the lanes of its feature pieces with one ds_bpermute.  out = acc / z.
+// and each edge-head weight p = e^(s-m') is computed once, by the lane that loaded s.
+// The chunk's weights (transposed to [head][edge]) and column ids are staged in a small
+// per-slot LDS area; each lane then reads its head's SC weights and the SC column ids with
+// vector LDS reads at immediate offsets.  out = acc / z.
 // In kLayer the score needs the gathered k row, so the maximum moves per group of U edges.
+//
+// Steps past a chunk's end use a column of the chunk (lanes past the end hold a clamped
+// column id) with weight 0, and each step's guard is a wave-uniform branch.
 //
 // A range result is the state (m[h], z[h], acc[h,:]); two states merge as
 //   m = max(m1, m2), z = z1 e^(m1-m) + z2 e^(m2-m), acc = acc1 e^(m1-m) + acc2 e^(m2-m).
@@ -23,16 +29,25 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace gat {
 
-template <typename T, int H, int D, int MODE>
+// Score dwords each lane loads per chunk: a chunk is kChunkLoads * G/H edges.
+constexpr int kChunkLoads = 1;
+
+template <typename T, int H, int D, int MODE, class TAB>
 struct Engine {
     using Gm = Geo<T, H, D>;
-    static constexpr int G = Gm::G, P = Gm::P, NV = Gm::NV, EPP = Gm::EPP, LPH = Gm::LPH, SC = Gm::SC,
-                         HD = Gm::HD;
-    static constexpr int UMAX = (8 / NV) > 1 ? (8 / NV) : 1;
+    static constexpr int G = Gm::G, P = Gm::P, NV = Gm::NV, EPP = Gm::EPP, LPH = Gm::LPH, HD = Gm::HD,
+                         RB = Gm::RB;
+    static constexpr int SM = kChunkLoads;          // score loads per lane per chunk
+    static constexpr int SC1 = Gm::SC;              // edges per score load (G/H)
+    static constexpr int SC = SM * SC1;             // edges per chunk
+    static constexpr int CM = (SC + G - 1) / G;     // column-id loads per lane per chunk
+    static constexpr int UMAX = (8 * SM / NV) > 1 ? (8 * SM / NV) : 1;
     static constexpr int U = SC < UMAX ? SC : UMAX;   // gathers in flight per lane per piece
 
     float acc[NV][EPP];
@@ -42,8 +57,12 @@ struct Engine {
     int hv[NV];                // head of piece v
     int off[NV];               // element offset of piece v inside a row
     int q, lane_base, es;
+    float* stage;              // this slot's LDS staging area: weights [H][SC], then column ids [SC]
 
-    __device__ __forceinline__ void init_lane(int lane) {
+    static constexpr int kStage = H * SC + SC;   // floats of staging per slot
+
+    __device__ __forceinline__ void init_lane(int lane, float* slot_stage) {
+        stage = slot_stage;
         q = lane % G;
         lane_base = lane - q;
         es = q / H;
@@ -67,22 +86,36 @@ struct Engine {
         z_s = 0.f;
     }
 
-    // Loads of one chunk [c, min(c+SC, e1)): scores (score layout) and column ids (lanes q < n).
-    __device__ __forceinline__ void load_chunk(const int32_t* __restrict__ col, const float* __restrict__ sc, int c,
-                                               int e1, float& s, int& cv) const {
-        const int n = (e1 - c) < SC ? (e1 - c) : SC;
-        s = 0.f;
-        cv = 0;
-        if (MODE != kLayer && es < n) s = sc[(int64_t)c * H + q];
-        if (q < n) cv = col[c + q];
+    __device__ __forceinline__ uint4 gather(const TAB& tab, int r, int v) const {
+        return tab.row16(r, (uint32_t)off[v] * (uint32_t)sizeof(T));
     }
 
-    __device__ __forceinline__ void load_q(const T* __restrict__ qrow) {
+    // Loads of one chunk [c, min(c+SC, e1)): scores (score layout, load k covers edges
+    // k*SC1 + q/H) and column ids (load k: edge k*G + q, clamped to the chunk's last edge, so
+    // steps past the chunk's end gather a row of the chunk).
+    __device__ __forceinline__ void load_chunk(const int32_t* __restrict__ col, const float* __restrict__ sc, int c,
+                                               int e1, float (&s)[SM], int (&cv)[CM]) const {
+        const int n = (e1 - c) < SC ? (e1 - c) : SC;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const uint4 t = ld16(qrow + off[v]);
-            unpack<T>(t, qf[v]);
+        for (int k = 0; k < SM; ++k) {
+            s[k] = 0.f;
+            if (MODE != kLayer && k * SC1 + es < n) s[k] = sc[(int64_t)(c + k * SC1) * H + q];
         }
+#pragma unroll
+        for (int k = 0; k < CM; ++k) {
+            const int i = k * G + q;
+            cv[k] = col[c + (i < n ? i : n - 1)];
+        }
+    }
+
+    __device__ __forceinline__ void load_q_raw(const T* __restrict__ qrow, uint4 (&raw)[NV]) const {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) raw[v] = ld16(qrow + off[v]);
+    }
+
+    __device__ __forceinline__ void set_q(const uint4 (&raw)[NV]) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) unpack<T>(raw[v], qf[v]);
     }
 
     __device__ __forceinline__ void fma_piece(int v, float w, const uint4& x) {
@@ -97,102 +130,130 @@ struct Engine {
         for (int k = 0; k < EPP; ++k) acc[v][k] *= c;
     }
 
-    // ---- kAgg / kSoftAgg: consume chunk [c, min(c+SC, e1)) with its loaded (s, cv); after the
-    // first gathers are issued, load the chunk at (nc, ne) into (s_n, cv_n) if nc < ne.
+    // ---- kAgg / kSoftAgg: consume chunk [c, min(c+SC, e1)) with its loaded (s, cv); first issue
+    // the loads of the chunk at (nc, ne) into (s_n, cv_n) when nc < ne.
     __device__ __forceinline__ void consume_scores(const int32_t* __restrict__ col, const float* __restrict__ sc,
-                                                   const T* __restrict__ feat, int c, int e1, float s, int cv,
-                                                   int nc, int ne, float& s_n, int& cv_n) {
+                                                   const TAB& vt, int c, int e1, const float (&s)[SM],
+                                                   const int (&cv)[CM], int nc, int ne, float (&s_n)[SM],
+                                                   int (&cv_n)[CM]) {
         const int n = (e1 - c) < SC ? (e1 - c) : SC;
-        float p;
+        float p[SM];
         if constexpr (MODE == kSoftAgg) {
-            const float sv = es < n ? s : -INFINITY;
-            float cm = sv;
+            float sv[SM];
+            float cm = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < SM; ++k) {
+                sv[k] = k * SC1 + es < n ? s[k] : -INFINITY;
+                cm = fmaxf(cm, sv[k]);
+            }
 #pragma unroll
             for (int k = H; k < G; k <<= 1) cm = fmaxf(cm, shfl_xor(cm, k));
             const float mo = m_s;
             const float mn = fmaxf(mo, cm);
             const float corr = exp_fast(mo - mn);   // 0 on the row's first chunk
             m_s = mn;
-            p = es < n ? exp_fast(sv - mn) : 0.f;
-            z_s = fmaf(z_s, corr, p);
+            float ps = 0.f;
+#pragma unroll
+            for (int k = 0; k < SM; ++k) {
+                p[k] = k * SC1 + es < n ? exp_fast(sv[k] - mn) : 0.f;
+                ps += p[k];
+            }
+            z_s = fmaf(z_s, corr, ps);
             if (__any(mo != -INFINITY && corr != 1.f)) {
 #pragma unroll
                 for (int v = 0; v < NV; ++v) scale_acc(v, shfl(corr, lane_base + hv[v]));
             }
         } else {
-            p = es < n ? s : 0.f;
+#pragma unroll
+            for (int k = 0; k < SM; ++k) p[k] = k * SC1 + es < n ? s[k] : 0.f;
         }
+        // weights transposed to [head][edge] and column ids into the slot's LDS area; LDS
+        // operations of one wave run in order, so the reads below see these writes.  Staged
+        // before the next chunk's loads are issued, so waiting for (s, cv) never waits on them.
+#pragma unroll
+        for (int k = 0; k < SM; ++k) stage[(q % H) * SC + k * SC1 + es] = p[k];
+#pragma unroll
+        for (int k = 0; k < CM; ++k)
+            if (k * G + q < SC) reinterpret_cast<int*>(stage)[H * SC + k * G + q] = cv[k];
+        if (nc < ne) load_chunk(col, sc, nc, ne, s_n, cv_n);
 #pragma unroll
         for (int jb = 0; jb < SC; jb += U) {
-            if (jb >= n) break;
+            if (!__any(jb < n)) break;
+            int cj[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) cj[u] = reinterpret_cast<const int*>(stage)[H * SC + jb + u];
             uint4 x[U][NV];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = jb + u;
-                const int cj = shfl(cv, lane_base + j);
-                const T* src = feat + (int64_t)cj * HD;
+                if (u == 0 || __any(jb + u < n)) {
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    if (j < n) x[u][v] = ld16(src + off[v]);
-                    else x[u][v] = make_uint4(0u, 0u, 0u, 0u);
+                    for (int v = 0; v < NV; ++v) x[u][v] = gather(vt, cj[u], v);
                 }
             }
-            if (jb == 0 && nc < ne) load_chunk(col, sc, nc, ne, s_n, cv_n);
+            float w[U][NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int u = 0; u < U; ++u) w[u][v] = stage[hv[v] * SC + jb + u];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = jb + u;
+                if (u == 0 || __any(jb + u < n)) {
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const float w = shfl(p, lane_base + j * H + hv[v]);
-                    if (j < n) fma_piece(v, w, x[u][v]);
+                    for (int v = 0; v < NV; ++v) fma_piece(v, w[u][v], x[u][v]);
                 }
             }
         }
     }
 
-    // ---- kLayer: consume chunk [c, min(c+SC, e1)) with its column ids cv (query in qf); after the
-    // first gathers are issued, load the column ids of the chunk at (nc, ne) into cv_n.
-    __device__ __forceinline__ void consume_layer(const int32_t* __restrict__ col, const T* __restrict__ kf,
-                                                  const T* __restrict__ vf, float scale, int c, int e1, int cv,
-                                                  int nc, int ne, int& cv_n) {
+    // ---- kLayer: consume chunk [c, min(c+SC, e1)) with its column ids cv (query in qf); first
+    // issue the column ids of the chunk at (nc, ne) into cv_n when nc < ne, and the query row
+    // qn into qraw_n when qn is not null.
+    __device__ __forceinline__ void consume_layer(const int32_t* __restrict__ col, const TAB& kt, const TAB& vt,
+                                                  float scale, int c, int e1, const int (&cv)[CM], int nc, int ne,
+                                                  int (&cv_n)[CM], const T* __restrict__ qn, uint4 (&qraw_n)[NV]) {
         const int n = (e1 - c) < SC ? (e1 - c) : SC;
 #pragma unroll
+        for (int k = 0; k < CM; ++k)
+            if (k * G + q < SC) reinterpret_cast<int*>(stage)[H * SC + k * G + q] = cv[k];
+        if (nc < ne) {
+            float unused[SM];
+            load_chunk(col, nullptr, nc, ne, unused, cv_n);
+        }
+        if (qn != nullptr) load_q_raw(qn, qraw_n);
+#pragma unroll
         for (int jb = 0; jb < SC; jb += U) {
-            if (jb >= n) break;
+            if (!__any(jb < n)) break;
+            int cj[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) cj[u] = reinterpret_cast<const int*>(stage)[H * SC + jb + u];
             uint4 kx[U][NV], vx[U][NV];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = jb + u;
-                const int cj = shfl(cv, lane_base + j);
-                const int64_t base = (int64_t)cj * HD;
+                if (u == 0 || __any(jb + u < n)) {
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    if (j < n) {
-                        kx[u][v] = ld16(kf + base + off[v]);
-                        vx[u][v] = ld16(vf + base + off[v]);
-                    } else {
-                        kx[u][v] = make_uint4(0u, 0u, 0u, 0u);
-                        vx[u][v] = make_uint4(0u, 0u, 0u, 0u);
+                    for (int v = 0; v < NV; ++v) {
+                        kx[u][v] = gather(kt, cj[u], v);
+                        vx[u][v] = gather(vt, cj[u], v);
                     }
                 }
-            }
-            if (jb == 0 && nc < ne) {
-                float unused;
-                load_chunk(col, nullptr, nc, ne, unused, cv_n);
             }
             float s[U][NV];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                const bool live = u == 0 || __any(jb + u < n);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    float f[EPP];
-                    unpack<T>(kx[u][v], f);
-                    float d = 0.f;
+                    s[u][v] = -INFINITY;
+                    if (live) {
+                        float f[EPP];
+                        unpack<T>(kx[u][v], f);
+                        float d = 0.f;
 #pragma unroll
-                    for (int k = 0; k < EPP; ++k) d = fmaf(qf[v][k], f[k], d);
+                        for (int k = 0; k < EPP; ++k) d = fmaf(qf[v][k], f[k], d);
 #pragma unroll
-                    for (int o = 1; o < LPH; o <<= 1) d += shfl_xor(d, o);
-                    s[u][v] = (jb + u < n) ? d * scale : -INFINITY;
+                        for (int o = 1; o < LPH; o <<= 1) d += shfl_xor(d, o);
+                        if (jb + u < n) s[u][v] = d * scale;
+                    }
                 }
             }
 #pragma unroll
@@ -207,9 +268,11 @@ struct Engine {
                 scale_acc(v, corr);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const float pw = exp_fast(s[u][v] - mn);
-                    z_p[v] += pw;
-                    fma_piece(v, pw, vx[u][v]);
+                    if (u == 0 || __any(jb + u < n)) {
+                        const float pw = exp_fast(s[u][v] - mn);
+                        z_p[v] += pw;
+                        fma_piece(v, pw, vx[u][v]);
+                    }
                 }
             }
         }
@@ -276,21 +339,31 @@ struct Engine {
 
     // Whole range [b, e) of one row as one chunk stream (segment kernels).
     __device__ __forceinline__ void run_range(const int32_t* __restrict__ col, const float* __restrict__ sc,
-                                              const T* __restrict__ qrow, const T* __restrict__ kf,
-                                              const T* __restrict__ vf, float scale, int b, int e) {
+                                              const T* __restrict__ qrow, const TAB& kt, const TAB& vt, float scale,
+                                              int b, int e) {
         reset();
         if (b >= e) return;
-        float s = 0.f;
-        int cv = 0;
+        float s[SM];
+        int cv[CM];
         load_chunk(col, sc, b, e, s, cv);
-        if constexpr (MODE == kLayer) load_q(qrow);
+        if constexpr (MODE == kLayer) {
+            uint4 raw[NV];
+            load_q_raw(qrow, raw);
+            set_q(raw);
+        }
         for (int c = b; c < e; c += SC) {
-            float s_n = 0.f;
-            int cv_n = 0;
-            if constexpr (MODE == kLayer) consume_layer(col, kf, vf, scale, c, e, cv, c + SC, e, cv_n);
-            else consume_scores(col, sc, vf, c, e, s, cv, c + SC, e, s_n, cv_n);
-            s = s_n;
-            cv = cv_n;
+            float s_n[SM] = {};
+            int cv_n[CM] = {};
+            if constexpr (MODE == kLayer) {
+                uint4 unused[NV];
+                consume_layer(col, kt, vt, scale, c, e, cv, c + SC, e, cv_n, nullptr, unused);
+            } else {
+                consume_scores(col, sc, vt, c, e, s, cv, c + SC, e, s_n, cv_n);
+            }
+#pragma unroll
+            for (int k = 0; k < SM; ++k) s[k] = s_n[k];
+#pragma unroll
+            for (int k = 0; k < CM; ++k) cv[k] = cv_n[k];
         }
         finish();
     }
@@ -303,22 +376,26 @@ struct Engine {
 // to the segment kernel and are skipped; short_max = INT_MAX without a plan.
 constexpr int kRowsPerWave = 32;
 
-template <typename T, int H, int D, int MODE>
+template <typename T, int H, int D, int MODE, class TAB>
 __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __restrict__ row_ptr,
                                                             const int32_t* __restrict__ col, int64_t n_rows,
-                                                            const float* __restrict__ sc, const T* __restrict__ qf,
-                                                            const T* __restrict__ kf, const T* __restrict__ vf,
-                                                            float scale, float* __restrict__ out, int short_max) {
-    using E = Engine<T, H, D, MODE>;
-    constexpr int P = E::P, G = E::G, HD = E::HD, SC = E::SC;
+                                                            int64_t n_src, const float* __restrict__ sc,
+                                                            const T* __restrict__ qf, const T* __restrict__ kf,
+                                                            const T* __restrict__ vf, float scale,
+                                                            float* __restrict__ out, int short_max) {
+    using E = Engine<T, H, D, MODE, TAB>;
+    constexpr int P = E::P, G = E::G, HD = E::HD, SC = E::SC, NV = E::NV, SM = E::SM, CM = E::CM;
     constexpr int RS = kRowsPerWave / P;   // rows per slot (<= G/2)
     static_assert(RS + 1 <= G, "a slot holds its rows' row_ptr entries");
     const int lane = lane_id();
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int64_t wb = wave * kRowsPerWave;
     if (wb >= n_rows) return;
+    __shared__ __align__(16) float stage[kWavesPerBlock * P * E::kStage];
+    const TAB vt(vf, n_src);
+    const TAB kt(MODE == kLayer ? kf : vf, n_src);
     E eng;
-    eng.init_lane(lane);
+    eng.init_lane(lane, stage + (threadIdx.x / kWave * P + lane / G) * E::kStage);
     const int q = eng.q, lb = eng.lane_base;
     const int64_t row0 = wb + (int64_t)(lane / G) * RS;
     int rpv = 0;
@@ -347,11 +424,15 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
     int e0 = 0, e1 = 0;
     int it = next_row(0, e0, e1);
     if (it >= RS) return;
-    float s = 0.f;
-    int cv = 0;
+    float s[SM];
+    int cv[CM];
     eng.reset();
     eng.load_chunk(col, sc, e0, e1, s, cv);
-    if constexpr (MODE == kLayer) eng.load_q(qf + (row0 + it) * HD);
+    if constexpr (MODE == kLayer) {
+        uint4 raw[NV];
+        eng.load_q_raw(qf + (row0 + it) * HD, raw);
+        eng.set_q(raw);
+    }
     int c = e0;
     while (true) {
         // successor chunk: the rest of this row, or the first chunk of the next non-empty row
@@ -362,22 +443,29 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
             nc = f0;
             ne = nit < RS ? f1 : f0;
         }
-        float s_n = 0.f;
-        int cv_n = 0;
-        if constexpr (MODE == kLayer) eng.consume_layer(col, kf, vf, scale, c, e1, cv, nc, ne, cv_n);
-        else eng.consume_scores(col, sc, vf, c, e1, s, cv, nc, ne, s_n, cv_n);
+        float s_n[SM] = {};
+        int cv_n[CM] = {};
+        uint4 qraw_n[NV];
+        if constexpr (MODE == kLayer) {
+            const T* qn = (nit != it && nit < RS) ? qf + (row0 + nit) * HD : nullptr;
+            eng.consume_layer(col, kt, vt, scale, c, e1, cv, nc, ne, cv_n, qn, qraw_n);
+        } else {
+            eng.consume_scores(col, sc, vt, c, e1, s, cv, nc, ne, s_n, cv_n);
+        }
         if (nit != it) {
             eng.finish();
             eng.store_row(out + (row0 + it) * HD, true);
             if (nit >= RS) break;
             eng.reset();
-            if constexpr (MODE == kLayer) eng.load_q(qf + (row0 + nit) * HD);
+            if constexpr (MODE == kLayer) eng.set_q(qraw_n);
             e1 = ne;
         }
         it = nit;
         c = nc;
-        s = s_n;
-        cv = cv_n;
+#pragma unroll
+        for (int k = 0; k < SM; ++k) s[k] = s_n[k];
+#pragma unroll
+        for (int k = 0; k < CM; ++k) cv[k] = cv_n[k];
     }
 }
 
@@ -386,28 +474,31 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
 // (persistent grid, counts read on the device).  The 4*P slots split the segment's edges into
 // contiguous sub-ranges, leave their states in LDS, and the workgroup merges them.  A long row
 // (slot < 0) is written out; a hub segment's state goes to the plan's partial buffer.
-template <typename T, int H, int D, int MODE>
-__global__ __launch_bounds__(kBlock) void spmm_segment_kernel(const int32_t* __restrict__ col,
+template <typename T, int H, int D, int MODE, class TAB>
+__global__ __launch_bounds__(kBlock) void spmm_segment_kernel(const int32_t* __restrict__ col, int64_t n_src,
                                                               const float* __restrict__ sc,
                                                               const T* __restrict__ qf, const T* __restrict__ kf,
                                                               const T* __restrict__ vf, float scale,
                                                               float* __restrict__ out, PlanView plan) {
-    using E = Engine<T, H, D, MODE>;
+    using E = Engine<T, H, D, MODE, TAB>;
     constexpr int NS = kWavesPerBlock * E::P;   // slots per workgroup
     constexpr int HD = E::HD;
     constexpr int SS = HD + 2 * H;              // floats per state
     __shared__ __align__(16) float lds[NS * SS];
+    __shared__ __align__(16) float stage[NS * E::kStage];
+    const TAB vt(vf, n_src);
+    const TAB kt(MODE == kLayer ? kf : vf, n_src);
     const int lane = lane_id();
     const int gs = (threadIdx.x / kWave) * E::P + lane / E::G;
     const int n_segs = plan.counts[kNSegs];
     E eng;
-    eng.init_lane(lane);
+    eng.init_lane(lane, stage + gs * E::kStage);
     for (int s = blockIdx.x; s < n_segs; s += gridDim.x) {
         const int4 sg = plan.segs[s];   // row, e_begin, e_end, slot
         const int64_t len = (int64_t)sg.z - sg.y;
         const int b = sg.y + (int)(len * gs / NS);
         const int e = sg.y + (int)(len * (gs + 1) / NS);
-        eng.run_range(col, sc, qf + (int64_t)sg.x * HD, kf, vf, scale, b, e);
+        eng.run_range(col, sc, qf + (int64_t)sg.x * HD, kt, vt, scale, b, e);
         eng.store_state(lds + gs * SS);
         __syncthreads();
         float* prt = sg.w >= 0 ? plan.partials + (int64_t)sg.w * plan.state_floats : nullptr;
@@ -473,23 +564,31 @@ __global__ __launch_bounds__(kBlock) void spmm_hub_merge_kernel(float* __restric
 
 template <int MODE>
 hipError_t launch_spmm_mode(int dtype, int H, int D, const int32_t* row_ptr, const int32_t* col, int64_t n_rows,
-                            const float* sc, const void* q, const void* k, const void* v, float scale,
+                            int64_t n_src, const float* sc, const void* q, const void* k, const void* v, float scale,
                             float* out, const PlanView* plan, hipStream_t stream) {
     const bool ok = dispatch_shape(dtype, H, D, [&](auto tag) {
         using Tag = decltype(tag);
         using T = typename Tag::type;
         constexpr int HH = Tag::H, DD = Tag::D;
+        constexpr int RB = Geo<T, HH, DD>::RB;
         const T* qt = static_cast<const T*>(q);
         const T* kt = static_cast<const T*>(k);
         const T* vt = static_cast<const T*>(v);
-        if (plan)
-            hipLaunchKernelGGL((spmm_segment_kernel<T, HH, DD, MODE>),
-                               dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
-                               col, sc, qt, kt, vt, scale, out, *plan);
         const int64_t waves = (n_rows + kRowsPerWave - 1) / kRowsPerWave;
         const unsigned blocks = grid_for(waves, kWavesPerBlock, INT32_MAX);
-        hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE>), dim3(blocks), dim3(kBlock), 0, stream, row_ptr,
-                           col, n_rows, sc, qt, kt, vt, scale, out, plan ? plan->short_max : INT32_MAX);
+        const int short_max = plan ? plan->short_max : INT32_MAX;
+        auto go = [&](auto tab_tag) {
+            using TAB = typename decltype(tab_tag)::type;
+            if (plan)
+                hipLaunchKernelGGL((spmm_segment_kernel<T, HH, DD, MODE, TAB>),
+                                   dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0,
+                                   stream, col, n_src, sc, qt, kt, vt, scale, out, *plan);
+            hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB>), dim3(blocks), dim3(kBlock), 0, stream,
+                               row_ptr, col, n_rows, n_src, sc, qt, kt, vt, scale, out, short_max);
+        };
+        // gathered tables below 4 GiB are read with 32-bit buffer offsets
+        if (n_src * (int64_t)RB <= (int64_t)UINT32_MAX) go(TypeTag<Tab32<RB>>{});
+        else go(TypeTag<Tab64<RB>>{});
     });
     if (!ok) return hipErrorInvalidValue;
     if (plan)

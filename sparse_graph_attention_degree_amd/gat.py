@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libgat.so")
 GAT_F32, GAT_BF16 = 0, 1
 STATUS = {0: "GAT_OK", 1: "GAT_ERR_NULL", 2: "GAT_ERR_SIZE", 3: "GAT_ERR_UNSUPPORTED", 4: "GAT_ERR_WORKSPACE",
           5: "GAT_ERR_ARGS", 6: "GAT_ERR_HIP"}
-DEFAULT_SHORT_MAX = 32
-DEFAULT_SEG_LEN = 2048
+DEFAULT_SHORT_MAX = 64
+DEFAULT_SEG_LEN = 1024
 
 EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge_softmax", "gat_aggregate",
             "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof"]
