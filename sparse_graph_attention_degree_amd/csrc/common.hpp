@@ -30,7 +30,9 @@ struct Elem<float> { static constexpr int bytes = 4; };
 template <>
 struct Elem<bf16_t> { static constexpr int bytes = 2; };
 
-template <typename T, int H_, int D_>
+// GMAX caps the slot width: narrower slots put more rows in flight per wave, each lane then
+// holding more pieces of its row.
+template <typename T, int H_, int D_, int GMAX = kWave>
 struct Geo {
     static constexpr int H = H_;
     static constexpr int D = D_;
@@ -38,7 +40,9 @@ struct Geo {
     static constexpr int S = Elem<T>::bytes;
     static constexpr int RB = HD * S;               // bytes per feature row
     static constexpr int NPC = RB / 16;             // 16-byte pieces per row
-    static constexpr int G = NPC < kWave ? NPC : kWave;   // lanes per slot
+    static constexpr int GW = GMAX < kWave ? GMAX : kWave;
+    static constexpr int G0 = NPC < GW ? NPC : GW;
+    static constexpr int G = G0 < H ? H : G0;       // lanes per slot (at least one per head)
     static constexpr int P = kWave / G;             // slots per wave
     static constexpr int NV = NPC / G;              // pieces per lane
     static constexpr int EPP = 16 / S;              // elements per piece

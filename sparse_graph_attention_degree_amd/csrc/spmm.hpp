@@ -38,9 +38,9 @@ namespace gat {
 // Score dwords each lane loads per chunk: a chunk is kChunkLoads * G/H edges.
 constexpr int kChunkLoads = 1;
 
-template <typename T, int H, int D, int MODE, class TAB>
+template <typename T, int H, int D, int MODE, class TAB, int GMAX = kWave>
 struct Engine {
-    using Gm = Geo<T, H, D>;
+    using Gm = Geo<T, H, D, GMAX>;
     static constexpr int G = Gm::G, P = Gm::P, NV = Gm::NV, EPP = Gm::EPP, LPH = Gm::LPH, HD = Gm::HD,
                          RB = Gm::RB;
     static constexpr int SM = kChunkLoads;          // score loads per lane per chunk
@@ -375,15 +375,17 @@ struct Engine {
 // single chunk stream (prefetching across row boundaries).  Rows with deg > short_max belong
 // to the segment kernel and are skipped; short_max = INT_MAX without a plan.
 constexpr int kRowsPerWave = 32;
+// Slot width of the short-row kernel (lanes per row in flight).
+constexpr int kShortSlotLanes = 32;
 
-template <typename T, int H, int D, int MODE, class TAB>
+template <typename T, int H, int D, int MODE, class TAB, int GMAX>
 __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __restrict__ row_ptr,
                                                             const int32_t* __restrict__ col, int64_t n_rows,
                                                             int64_t n_src, const float* __restrict__ sc,
                                                             const T* __restrict__ qf, const T* __restrict__ kf,
                                                             const T* __restrict__ vf, float scale,
                                                             float* __restrict__ out, int short_max) {
-    using E = Engine<T, H, D, MODE, TAB>;
+    using E = Engine<T, H, D, MODE, TAB, GMAX>;
     constexpr int P = E::P, G = E::G, HD = E::HD, SC = E::SC, NV = E::NV, SM = E::SM, CM = E::CM;
     constexpr int RS = kRowsPerWave / P;   // rows per slot (<= G/2)
     static_assert(RS + 1 <= G, "a slot holds its rows' row_ptr entries");
@@ -583,7 +585,8 @@ hipError_t launch_spmm_mode(int dtype, int H, int D, const int32_t* row_ptr, con
                 hipLaunchKernelGGL((spmm_segment_kernel<T, HH, DD, MODE, TAB>),
                                    dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0,
                                    stream, col, n_src, sc, qt, kt, vt, scale, out, *plan);
-            hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB>), dim3(blocks), dim3(kBlock), 0, stream,
+            hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB, kShortSlotLanes>), dim3(blocks),
+                               dim3(kBlock), 0, stream,
                                row_ptr, col, n_rows, n_src, sc, qt, kt, vt, scale, out, short_max);
         };
         // gathered tables below 4 GiB are read with 32-bit buffer offsets

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 64, "f32"), (8, 32, "f32"), (4, 64, "bf16"), (8, 16, "f32"), (1, 128, "f32"), (2, 16, "bf16"),
           (16, 64, "f32"), (8, 128, "bf16"), (1, 16, "f32")]
-SCHEDULES = [None, (-1, 0), (0, 1), (0, 3), (1, 7), (5, 64), (64, 200)]
+SCHEDULES = [None, (-1, 0), (0, 1), (0, 3), (1, 7), (5, 64), (64, 200), (3000, 4096)]
 
 
 @pytest.fixture(scope="module")
