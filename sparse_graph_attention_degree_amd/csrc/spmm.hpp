@@ -536,30 +536,98 @@ __global__ __launch_bounds__(kBlock) void spmm_segment_kernel(const int32_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
-// Hub rows: merge the states of a row's segments and write the row.
-template <int MODE>
+// Hub rows: merge the states of a row's segments and write the row.  One workgroup per hub row.
+//  1. per-head max and sum: the 256 threads split the segments and merge (m, z) pairs, then an
+//     xor-shuffle tree and a 4-wave merge through LDS give M[h], Z[h];
+//  2. acc: thread groups split the segments (groups = 256 / (H*D) when H*D < 256), each thread
+//     owning one element per group, with coalesced loads of the segments' acc rows and unrolled
+//     loops; the groups' sums meet in LDS.
+template <int MODE, int HMAX>
 __global__ __launch_bounds__(kBlock) void spmm_hub_merge_kernel(float* __restrict__ out, int H, int D,
                                                                 PlanView plan) {
+    __shared__ float lm[kWavesPerBlock][HMAX], lz[kWavesPerBlock][HMAX];
+    __shared__ float gM[HMAX], gZ[HMAX];
+    __shared__ float part[kBlock];
     const int HD = H * D;
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const int groups = HD < kBlock ? kBlock / HD : 1;
+    const int g = HD < kBlock ? t / HD : 0;
+    const int64_t sf = plan.state_floats;
     const int n_hubs = plan.counts[kNHubs];
     for (int hb = blockIdx.x; hb < n_hubs; hb += gridDim.x) {
         const int4 hr = plan.hubs[hb];   // row, first segment, n segments
-        for (int el = threadIdx.x; el < HD; el += kBlock) {
-            const int h = el / D;
-            const float* p0 = plan.partials + (int64_t)hr.y * plan.state_floats;
-            float M = -INFINITY, Z = 0.f, A = 0.f;
-            if (MODE != kAgg)
-                for (int c = 0; c < hr.z; ++c) M = fmaxf(M, p0[(int64_t)c * plan.state_floats + h]);
-            for (int c = 0; c < hr.z; ++c) {
-                const float* pc = p0 + (int64_t)c * plan.state_floats;
-                float w = 1.f;
-                if (MODE != kAgg) {
-                    w = (pc[h] == -INFINITY) ? 0.f : exp_fast(pc[h] - M);
-                    Z = fmaf(pc[H + h], w, Z);
-                }
-                A = fmaf(pc[2 * H + el], w, A);
+        const float* p0 = plan.partials + (int64_t)hr.y * sf;
+        if constexpr (MODE != kAgg) {
+            float m[HMAX], z[HMAX];
+#pragma unroll
+            for (int h = 0; h < HMAX; ++h) {
+                m[h] = -INFINITY;
+                z[h] = 0.f;
             }
-            out[(int64_t)hr.x * HD + el] = (MODE == kAgg) ? A : A / Z;
+            for (int c = t; c < hr.z; c += kBlock) {
+                const float* pc = p0 + (int64_t)c * sf;
+#pragma unroll
+                for (int h = 0; h < HMAX; ++h) {
+                    if (h < H) {
+                        const float mc = pc[h], zc = pc[H + h];
+                        const float mn = fmaxf(m[h], mc);
+                        z[h] = (m[h] == -INFINITY ? 0.f : z[h] * exp_fast(m[h] - mn)) +
+                               (mc == -INFINITY ? 0.f : zc * exp_fast(mc - mn));
+                        m[h] = mn;
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < HMAX; ++h) {
+                if (h < H) {
+#pragma unroll
+                    for (int o = 1; o < kWave; o <<= 1) {
+                        const float mo = shfl_xor(m[h], o), zo = shfl_xor(z[h], o);
+                        const float mn = fmaxf(m[h], mo);
+                        z[h] = (m[h] == -INFINITY ? 0.f : z[h] * exp_fast(m[h] - mn)) +
+                               (mo == -INFINITY ? 0.f : zo * exp_fast(mo - mn));
+                        m[h] = mn;
+                    }
+                    if (lane == 0) {
+                        lm[w][h] = m[h];
+                        lz[w][h] = z[h];
+                    }
+                }
+            }
+            __syncthreads();
+            if (t < H) {
+                float M = -INFINITY, Z = 0.f;
+#pragma unroll
+                for (int i = 0; i < kWavesPerBlock; ++i) M = fmaxf(M, lm[i][t]);
+#pragma unroll
+                for (int i = 0; i < kWavesPerBlock; ++i)
+                    if (lm[i][t] != -INFINITY) Z = fmaf(lz[i][t], exp_fast(lm[i][t] - M), Z);
+                gM[t] = M;
+                gZ[t] = Z;
+            }
+            __syncthreads();
+        }
+        for (int el0 = 0; el0 < HD; el0 += kBlock) {
+            const int el = el0 + (HD < kBlock ? t % HD : t);
+            const bool live = el < HD && g < groups;
+            const int h = live ? el / D : 0;
+            const float M = (MODE != kAgg) ? gM[h] : 0.f;
+            float A = 0.f;
+            if (live) {
+#pragma unroll 8
+                for (int c = g; c < hr.z; c += groups) {
+                    const float* pc = p0 + (int64_t)c * sf;
+                    const float wgt = (MODE != kAgg) ? (pc[h] == -INFINITY ? 0.f : exp_fast(pc[h] - M)) : 1.f;
+                    A = fmaf(pc[2 * H + el], wgt, A);
+                }
+            }
+            part[t] = A;
+            __syncthreads();
+            if (live && g == 0) {
+                for (int i = 1; i < groups; ++i) A += part[i * HD + (t % HD)];
+                out[(int64_t)hr.x * HD + el] = (MODE == kAgg) ? A : A / gZ[h];
+            }
+            __syncthreads();
         }
     }
 }
@@ -595,7 +663,7 @@ hipError_t launch_spmm_mode(int dtype, int H, int D, const int32_t* row_ptr, con
     });
     if (!ok) return hipErrorInvalidValue;
     if (plan)
-        hipLaunchKernelGGL(spmm_hub_merge_kernel<MODE>, dim3(grid_for(plan->hub_capacity, 1, kPersistentBlocks)),
+        hipLaunchKernelGGL((spmm_hub_merge_kernel<MODE, 16>), dim3(grid_for(plan->hub_capacity, 1, kPersistentBlocks)),
                            dim3(kBlock), 0, stream, out, H, D, *plan);
     return hipGetLastError();
 }
