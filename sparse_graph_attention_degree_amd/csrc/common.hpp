@@ -61,6 +61,27 @@ __device__ __forceinline__ int shfl(int v, int src) { return __shfl(v, src); }
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask); }
 __device__ __forceinline__ int shfl_xor(int v, int mask) { return __shfl_xor(v, mask); }
 
+// DPP move within the wave (row_mask = bank_mask = 0xF; every source lane below is valid).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of N consecutive lanes (N a power of two <= 64); every lane of
+// the group receives the sum.  Up to 16 lanes it stays in registers (DPP): two quad
+// permutations give the quad sum, the half-row mirror (lane i <-> 7-i) adds the other quad,
+// the row mirror (lane i <-> 15-i) adds the other half-row; wider groups use shuffles.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (N >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror
+    if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
+    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
 // e^x as the hardware exp2 of x*log2(e).  exp(-inf) = 0.
 __device__ __forceinline__ float exp_fast(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);

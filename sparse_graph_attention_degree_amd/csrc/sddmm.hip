@@ -6,7 +6,7 @@
 // over the 128 features and a shuffle tree.  Here a slot of G lanes (common.hpp)
 // owns one edge and each lane takes 16-byte pieces of both rows, so one wave64
 // holds P edges per step and U steps of gathers are issued before any is used.
-// The per-head sum is an xor-shuffle tree over the LPH lanes of a head.  The waves
+// The per-head sum over the LPH lanes of a head stays in registers (DPP, group_sum).  The waves
 // sweep the edge list together (grid-stride), so with edges sorted by destination
 // neighbouring waves share destination rows and output lines in L2; keeping the
 // destination row in registers across repeated destinations, prefetching the next
@@ -71,8 +71,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t* __restrict
                 float d = 0.f;
 #pragma unroll
                 for (int k = 0; k < EPP; ++k) d = fmaf(fa[k], fb[k], d);
-#pragma unroll
-                for (int o = 1; o < LPH; o <<= 1) d += shfl_xor(d, o);
+                d = group_sum<LPH>(d);
                 if (e < n_edges && (v * G + q) % LPH == 0) out[e * H + hv[v]] = scale * d;
             }
         }

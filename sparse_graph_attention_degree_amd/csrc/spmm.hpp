@@ -250,8 +250,7 @@ struct Engine {
                         float d = 0.f;
 #pragma unroll
                         for (int k = 0; k < EPP; ++k) d = fmaf(qf[v][k], f[k], d);
-#pragma unroll
-                        for (int o = 1; o < LPH; o <<= 1) d += shfl_xor(d, o);
+                        d = group_sum<LPH>(d);
                         if (jb + u < n) s[u][v] = d * scale;
                     }
                 }
