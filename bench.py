@@ -16,7 +16,9 @@ its mean duration measured with HIP events on the launch stream.  ``traffic`` is
 the HBM byte count of the same call from rocprofv3 FETCH_SIZE + WRITE_SIZE
 (profiles/), scaled by a plain-copy calibration, or null when the kernel sources
 changed since the counters were taken.  ``cpu_baseline`` times the CPU oracle on a
-bounded prefix of the same graph.
+bounded prefix of the same graph (every host thread, and one thread).  ``extra`` holds the
+other rows of the path timed alone, the unique-bytes lower bound of the fused call and a
+streaming device copy measured on the same GPU.
 
 The COO workload c2 (1024 x 128 / 768 x 128 fp32 tables, 16384 edges) has no CSR: its step is
 the SDDMM alone and its roofline is the SDDMM's.
@@ -91,26 +93,56 @@ def copy_calibration(nbytes=1 << 30, reps=3):
                       "calls": reps}))
 
 
-def cpu_baseline(g, w, q, k, v, budget_s=12.0):
-    """The oracle's full layer on a prefix of the graph, grown until it takes ~budget_s."""
+def cpu_baseline(g, w, q, k, v, budget_s=12.0, one_thread_s=4.0):
+    """The oracle's full layer on a prefix of the graph, grown until it takes ~budget_s on every
+    host thread; then a smaller prefix on one thread (~one_thread_s)."""
     import oracle
     from sparse_graph_attention_degree_amd import graphs as G
     orc = oracle.get()
-    target_edges = 1 << 15
-    while True:
-        rows = int(np.searchsorted(g.row_ptr, target_edges))
-        rows = max(1, min(rows, g.n_rows))
-        sub_rp, sub_col, _ = G.take_rows(g, np.arange(rows))
-        t0 = time.perf_counter()
-        orc.layer(sub_rp, sub_col, q[:rows], k, v)
-        dt = time.perf_counter() - t0
-        e = int(sub_rp[-1])
-        if dt >= budget_s / 4 or rows == g.n_rows:
-            break
-        target_edges = int(target_edges * min(16.0, max(2.0, budget_s / max(dt, 1e-3))))
-    return {"value": e * w.heads / dt, "unit": "edge-heads/s", "cores": orc.num_threads(), "kind": "oracle",
+
+    def run_prefix(target_edges, budget):
+        while True:
+            rows = int(np.searchsorted(g.row_ptr, target_edges))
+            rows = max(1, min(rows, g.n_rows))
+            sub_rp, sub_col, _ = G.take_rows(g, np.arange(rows))
+            t0 = time.perf_counter()
+            orc.layer(sub_rp, sub_col, q[:rows], k, v)
+            dt = time.perf_counter() - t0
+            e = int(sub_rp[-1])
+            if dt >= budget / 4 or rows == g.n_rows:
+                return rows, e, dt
+            target_edges = int(target_edges * min(16.0, max(2.0, budget / max(dt, 1e-3))))
+
+    threads = orc.num_threads()
+    rows, e, dt = run_prefix(1 << 15, budget_s)
+    orc.set_num_threads(1)
+    try:
+        rows1, e1, dt1 = run_prefix(1 << 12, one_thread_s)
+    finally:
+        orc.set_num_threads(threads)
+    return {"value": e * w.heads / dt, "unit": "edge-heads/s", "cores": threads, "kind": "oracle",
             "sample": f"full layer (sddmm + softmax + aggregate, fp64) on the first {rows} rows "
-                      f"({e} edges) of the same graph, {dt:.2f} s"}
+                      f"({e} edges) of the same graph, {dt:.2f} s",
+            "one_thread": {"value": e1 * w.heads / dt1, "unit": "edge-heads/s", "cores": 1,
+                           "sample": f"the first {rows1} rows ({e1} edges), {dt1:.2f} s"}}
+
+
+def copy_rate(nbytes=1 << 30, reps=5):
+    """Streaming device copy (torch copy_, read + write bytes per second) on this GPU."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    return 2 * nbytes / t / 1e9
 
 
 def bench_coo(args, w, gat, G):
@@ -255,12 +287,23 @@ def main():
     achieved = alg / t_fused / 1e9
     traffic = read_traffic(args.workload)
 
+    # lower bound: every distinct source row read once (the rest as in the algorithmic count)
+    n_distinct = int(np.count_nonzero(np.bincount(g.col_idx, minlength=g.n_src))) if E else 0
+    unique = alg - E * H * D * feat_bytes + n_distinct * H * D * feat_bytes
     extra = {"t_plan_ms": t_plan * 1e3, "t_sddmm_ms": t_sddmm * 1e3, "t_fused_ms": t_fused * 1e3,
              "fused_edge_heads_per_s": E * H / t_fused,
              "fused_alg_bytes": alg,
+             "fused_unique_bytes": unique,
+             "fused_unique_gbs": unique / t_fused / 1e9,
              "sddmm_alg_bytes": 8 * E + 2 * E * H * D * feat_bytes + 4 * E * H,
              "sddmm_gbs": (8 * E + 2 * E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
+             # the destination rows repeat along each CSR row and stay in cache: gathered k rows only
+             "sddmm_k_gather_gbs": (8 * E + E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
              "kernel_source_sha256": kernel_source_digest()}
+    if not args.no_extra:
+        cp = copy_rate()
+        extra["copy_gbs"] = cp
+        extra["fused_frac_of_copy"] = achieved / cp
 
     if not args.no_extra:
         # the other rows of the path, each timed alone over the same graph (5 calls, HIP events)

@@ -57,6 +57,8 @@ class Oracle:
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         L = self.lib
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
+        L.oracle_set_num_threads.restype = None
         L.oracle_sddmm.argtypes = [i64, vp, vp, vp, vp, i32, i32, i32, dbl, vp]
         L.oracle_edge_softmax.argtypes = [i64, vp, i32, vp, vp]
         L.oracle_aggregate.argtypes = [i64, vp, vp, i32, i32, vp, vp, i32, vp]
@@ -68,6 +70,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.oracle_set_num_threads(int(n))
 
     # --- steps -------------------------------------------------------------------------
     def sddmm(self, src_idx, dst_idx, src_feat, dst_feat, scale: float = 1.0) -> np.ndarray:

@@ -75,6 +75,16 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following calls (benchmark use: the one-thread CPU figure). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * SDDMM over an edge list [l1_p10]:
  *   out[e,h] = scale * sum_d dst_feat[dst_idx[e],h,d] * src_feat[src_idx[e],h,d]
