@@ -120,11 +120,24 @@ def cpu_baseline(g, w, q, k, v, budget_s=12.0, one_thread_s=4.0):
         rows1, e1, dt1 = run_prefix(1 << 12, one_thread_s)
     finally:
         orc.set_num_threads(threads)
-    return {"value": e * w.heads / dt, "unit": "edge-heads/s", "cores": threads, "kind": "oracle",
+    return {"value": e * w.heads / dt, "unit": "edge-heads/s", "cores": threads, "kind": "oracle", "host": host_cpu(),
             "sample": f"full layer (sddmm + softmax + aggregate, fp64) on the first {rows} rows "
                       f"({e} edges) of the same graph, {dt:.2f} s",
             "one_thread": {"value": e1 * w.heads / dt1, "unit": "edge-heads/s", "cores": 1,
                            "sample": f"the first {rows1} rows ({e1} edges), {dt1:.2f} s"}}
+
+
+def host_cpu():
+    """Host CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def copy_rate(nbytes=1 << 30, reps=5):
@@ -167,6 +180,14 @@ def bench_coo(args, w, gat, G):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     t_k = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    # launch-bound size: 1000 back-to-back calls timed as one interval
+    a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(1000):
+        gat.gat_sddmm(sid, did, sfd, dfd, out=out)
+    b0.record(stream)
+    torch.cuda.synchronize()
+    t_b2b_us = a0.elapsed_time(b0)
     alg = 8 * E + 2 * E * H * D * 4 + 4 * E * H
     cpu = None
     if not args.no_cpu:
@@ -178,6 +199,7 @@ def bench_coo(args, w, gat, G):
             reps += 1
         dt = (time.perf_counter() - t1) / reps
         cpu = {"value": E * H / dt, "unit": "edge-heads/s", "cores": orc.num_threads(), "kind": "oracle",
+               "host": host_cpu(),
                "sample": f"the whole edge list ({E} edges), {reps} repetitions"}
     print(json.dumps({
         "metric": METRIC, "value": E * H / (elapsed / args.steps), "unit": "edge-heads/s", "n_gpus": 1,
@@ -188,7 +210,7 @@ def bench_coo(args, w, gat, G):
         "roofline": {"bound": "hbm", "achieved": alg / t_k / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": alg / t_k / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "sddmm (launch-bound size)"},
         "cpu_baseline": cpu,
-        "extra": {"t_sddmm_ms": t_k * 1e3, "sddmm_alg_bytes": alg},
+        "extra": {"t_sddmm_ms": t_k * 1e3, "sddmm_alg_bytes": alg, "sddmm_back_to_back_us": t_b2b_us},
     }))
 
 
@@ -290,7 +312,9 @@ def main():
     # lower bound: every distinct source row read once (the rest as in the algorithmic count)
     n_distinct = int(np.count_nonzero(np.bincount(g.col_idx, minlength=g.n_src))) if E else 0
     unique = alg - E * H * D * feat_bytes + n_distinct * H * D * feat_bytes
+    fused_ms = [e[2].elapsed_time(e[3]) for e in ev]
     extra = {"t_plan_ms": t_plan * 1e3, "t_sddmm_ms": t_sddmm * 1e3, "t_fused_ms": t_fused * 1e3,
+             "t_fused_median_ms": float(np.median(fused_ms)), "t_fused_min_ms": float(np.min(fused_ms)),
              "fused_edge_heads_per_s": E * H / t_fused,
              "fused_alg_bytes": alg,
              "fused_unique_bytes": unique,
@@ -300,6 +324,17 @@ def main():
              # the destination rows repeat along each CSR row and stay in cache: gathered k rows only
              "sddmm_k_gather_gbs": (8 * E + E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
              "kernel_source_sha256": kernel_source_digest()}
+    if E * H < (1 << 22):
+        # launch-bound sizes: 1000 back-to-back planned fused calls timed as one interval
+        plan = gat.gat_plan_build(rp, E, H, D, ws=ws)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(1000):
+            gat.gat_fused_layer(rp, col, vd, scores=scores, out=out, plan=plan)
+        b.record(stream)
+        torch.cuda.synchronize()
+        extra["fused_back_to_back_us"] = a.elapsed_time(b)  # ms for 1000 calls = us per call
     if not args.no_extra:
         cp = copy_rate()
         extra["copy_gbs"] = cp

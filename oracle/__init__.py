@@ -64,8 +64,13 @@ class Oracle:
         L.oracle_aggregate.argtypes = [i64, vp, vp, i32, i32, vp, vp, i32, vp]
         L.oracle_softmax_aggregate.argtypes = [i64, vp, vp, i32, i32, vp, vp, i32, vp]
         L.oracle_layer.argtypes = [i64, vp, vp, i32, i32, vp, vp, vp, i32, dbl, vp]
+        L.oracle_edge_softmax_backward.argtypes = [i64, vp, i32, vp, vp, vp]
+        L.oracle_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
+        L.oracle_softmax_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
+        L.oracle_layer_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp]
         for f in (L.oracle_sddmm, L.oracle_edge_softmax, L.oracle_aggregate,
-                  L.oracle_softmax_aggregate, L.oracle_layer):
+                  L.oracle_softmax_aggregate, L.oracle_layer, L.oracle_edge_softmax_backward,
+                  L.oracle_aggregate_backward, L.oracle_softmax_aggregate_backward, L.oracle_layer_backward):
             f.restype = i32
 
     def num_threads(self) -> int:
@@ -138,6 +143,72 @@ class Oracle:
                                    _dtype_code(v), float(scale), _p(out))
         assert rc == 0
         return out
+
+
+    # --- backward (derivatives of the steps above) --------------------------------------
+    def edge_softmax_backward(self, row_ptr, alpha, grad) -> np.ndarray:
+        """dL/dscores from the softmax output alpha and dL/dalpha, both [E,H]."""
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        alpha = np.ascontiguousarray(alpha, np.float64)
+        grad = np.ascontiguousarray(grad, np.float64)
+        E, H = alpha.shape
+        assert grad.shape == (E, H) and row_ptr[-1] == E
+        out = np.full((E, H), np.nan, np.float64)
+        rc = self.lib.oracle_edge_softmax_backward(row_ptr.size - 1, _p(row_ptr), H, _p(alpha), _p(grad), _p(out))
+        assert rc == 0
+        return out
+
+    def aggregate_backward(self, row_ptr, col_idx, weights, feat, grad):
+        """(dL/dweights [E,H], dL/dfeat [n_src,H,D]) from dL/dout [N,H,D]."""
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        col_idx = np.ascontiguousarray(col_idx, np.int32)
+        weights = np.ascontiguousarray(weights, np.float64)
+        feat = np.ascontiguousarray(feat)
+        grad = np.ascontiguousarray(grad, np.float64)
+        ns, H, D = feat.shape
+        n = row_ptr.size - 1
+        assert grad.shape == (n, H, D)
+        dw = np.full(weights.shape, np.nan, np.float64)
+        df = np.full((ns, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_aggregate_backward(n, _p(row_ptr), _p(col_idx), H, D, ns, _p(weights), _p(feat),
+                                                _dtype_code(feat), _p(grad), _p(dw), _p(df))
+        assert rc == 0
+        return dw, df
+
+    def softmax_aggregate_backward(self, row_ptr, col_idx, scores, feat, grad):
+        """(dL/dscores [E,H], dL/dfeat [n_src,H,D]) of softmax + aggregation."""
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        col_idx = np.ascontiguousarray(col_idx, np.int32)
+        scores = np.ascontiguousarray(scores, np.float64)
+        feat = np.ascontiguousarray(feat)
+        grad = np.ascontiguousarray(grad, np.float64)
+        ns, H, D = feat.shape
+        n = row_ptr.size - 1
+        assert grad.shape == (n, H, D)
+        ds = np.full(scores.shape, np.nan, np.float64)
+        df = np.full((ns, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_softmax_aggregate_backward(n, _p(row_ptr), _p(col_idx), H, D, ns, _p(scores), _p(feat),
+                                                        _dtype_code(feat), _p(grad), _p(ds), _p(df))
+        assert rc == 0
+        return ds, df
+
+    def layer_backward(self, row_ptr, col_idx, q, k, v, grad, scale: float = 1.0):
+        """(dL/dq [N,H,D], dL/dk [n_src,H,D], dL/dv [n_src,H,D]) of the full layer."""
+        row_ptr = np.ascontiguousarray(row_ptr, np.int32)
+        col_idx = np.ascontiguousarray(col_idx, np.int32)
+        q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+        grad = np.ascontiguousarray(grad, np.float64)
+        assert q.dtype == k.dtype == v.dtype
+        ns, H, D = v.shape
+        n = row_ptr.size - 1
+        assert q.shape == (n, H, D) and k.shape == (ns, H, D) and grad.shape == (n, H, D)
+        dq = np.full((n, H, D), np.nan, np.float64)
+        dk = np.full((ns, H, D), np.nan, np.float64)
+        dv = np.full((ns, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_layer_backward(n, _p(row_ptr), _p(col_idx), H, D, ns, _p(q), _p(k), _p(v),
+                                            _dtype_code(v), float(scale), _p(grad), _p(dq), _p(dk), _p(dv))
+        assert rc == 0
+        return dq, dk, dv
 
 
 _default = None

@@ -22,6 +22,8 @@
  *            keep their zero output.
  * The full layer (scores from q_i . k_j, then softmax, then aggregation of v)
  * is the composition of the three steps above; no single page writes it out.
+ * The backward functions at the end are the derivatives of these definitions
+ * (chain rule); no page writes them out either.
  *
  * Precision: every floating-point input is widened exactly to double (bf16 is
  * decoded bit-exactly) and all arithmetic is double; results are returned as
@@ -199,4 +201,155 @@ int oracle_layer(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
     free(dst);
     free(scores);
     return rc;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Backward.  No page writes the backward pass out; the l1_p10 page (edge-only SDDMM) notes that
+ * gradients flow back to rows of the feature tables, summed over the edges that read each row.
+ * Each function below is the derivative of the forward definition above it (chain rule), as
+ * plain loops in double precision.  grad arguments are dL/d(output) of the forward step.
+ * ------------------------------------------------------------------------------------------ */
+
+/*
+ * Edge softmax backward: for every row i with edges and every head h, with a = softmax output
+ * and g = dL/da over the row's edges:
+ *   out[e,h] = a[e,h] * (g[e,h] - sum_{e' in row i} a[e',h] * g[e',h])
+ * (the softmax Jacobian diag(a) - a a^T applied to g).
+ */
+int oracle_edge_softmax_backward(int64_t n_rows, const int32_t* row_ptr, int heads,
+                                 const double* alpha, const double* grad, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t start = row_ptr[i], end = row_ptr[i + 1];
+        for (int h = 0; h < heads; ++h) {
+            double dot = 0.0;
+            for (int64_t e = start; e < end; ++e)
+                dot += alpha[e * heads + h] * grad[e * heads + h];
+            for (int64_t e = start; e < end; ++e)
+                out[e * heads + h] = alpha[e * heads + h] * (grad[e * heads + h] - dot);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Aggregation backward, g = dL/dout [n_rows,heads,head_dim]:
+ *   dweights[e,h] = sum_d g[i,h,d] * feat[col_idx[e],h,d]            (e in row i)
+ *   dfeat[j,h,d]  = sum over edges e with col_idx[e] = j of weights[e,h] * g[row of e,h,d]
+ * dfeat is [n_src,heads,head_dim] and starts at 0.0 (sources no edge reads stay +0.0); its sums
+ * visit the edges in increasing edge id.  Threads split the heads, so no two write one value.
+ */
+int oracle_aggregate_backward(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                              int heads, int head_dim, int64_t n_src, const double* weights,
+                              const void* feat, int dtype, const double* grad,
+                              double* dweights, double* dfeat)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            for (int h = 0; h < heads; ++h) {
+                double acc = 0.0;
+                for (int d = 0; d < head_dim; ++d)
+                    acc += grad[(i * heads + h) * head_dim + d] *
+                           load_feat(feat, dtype, ((int64_t)col_idx[e] * heads + h) * head_dim + d);
+                dweights[e * heads + h] = acc;
+            }
+        }
+    }
+    for (int64_t x = 0; x < n_src * heads * head_dim; ++x)
+        dfeat[x] = 0.0;
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < heads; ++h) {
+        for (int64_t i = 0; i < n_rows; ++i) {
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                int64_t j = col_idx[e];
+                for (int d = 0; d < head_dim; ++d)
+                    dfeat[(j * heads + h) * head_dim + d] += weights[e * heads + h] * grad[(i * heads + h) * head_dim + d];
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Softmax + aggregation backward: a = softmax(scores); (g_a, dfeat) = aggregation backward of
+ * a and feat; dscores = softmax backward of (a, g_a).
+ */
+int oracle_softmax_aggregate_backward(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                                      int heads, int head_dim, int64_t n_src, const double* scores,
+                                      const void* feat, int dtype, const double* grad,
+                                      double* dscores, double* dfeat)
+{
+    int64_t n_edges = row_ptr[n_rows];
+    size_t ne = (size_t)(n_edges > 0 ? n_edges : 1) * heads;
+    double* alpha = (double*)malloc(ne * sizeof(double));
+    double* ga = (double*)malloc(ne * sizeof(double));
+    if (!alpha || !ga) { free(alpha); free(ga); return 1; }
+    oracle_edge_softmax(n_rows, row_ptr, heads, scores, alpha);
+    oracle_aggregate_backward(n_rows, row_ptr, col_idx, heads, head_dim, n_src, alpha, feat, dtype, grad, ga, dfeat);
+    oracle_edge_softmax_backward(n_rows, row_ptr, heads, alpha, ga, dscores);
+    free(alpha);
+    free(ga);
+    return 0;
+}
+
+/*
+ * Full layer backward (q [n_rows,H,D]; k, v [n_src,H,D]), with s = scale * <q_i, k_j>,
+ * a = softmax(s) per row, out_i = sum_e a[e] v_j:
+ *   (g_a, dv) = aggregation backward of (a, v, g)
+ *   g_s       = softmax backward of (a, g_a)
+ *   dq[i]     = scale * sum_{e in row i} g_s[e] * k[col_idx[e]]
+ *   dk[j]     = scale * sum over edges e with col_idx[e] = j of g_s[e] * q[row of e]
+ * per head.  dk and dv start at 0.0.
+ */
+int oracle_layer_backward(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                          int heads, int head_dim, int64_t n_src, const void* q, const void* k,
+                          const void* v, int dtype, double scale, const double* grad,
+                          double* dq, double* dk, double* dv)
+{
+    int64_t n_edges = row_ptr[n_rows];
+    size_t ne = (size_t)(n_edges > 0 ? n_edges : 1);
+    int32_t* row_of = (int32_t*)malloc(ne * sizeof(int32_t));
+    double* s = (double*)malloc(ne * heads * sizeof(double));
+    double* a = (double*)malloc(ne * heads * sizeof(double));
+    double* ga = (double*)malloc(ne * heads * sizeof(double));
+    double* gs = (double*)malloc(ne * heads * sizeof(double));
+    if (!row_of || !s || !a || !ga || !gs) { free(row_of); free(s); free(a); free(ga); free(gs); return 1; }
+    for (int64_t i = 0; i < n_rows; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e)
+            row_of[e] = (int32_t)i;
+    oracle_sddmm(n_edges, col_idx, row_of, k, q, dtype, heads, head_dim, scale, s);
+    oracle_edge_softmax(n_rows, row_ptr, heads, s, a);
+    oracle_aggregate_backward(n_rows, row_ptr, col_idx, heads, head_dim, n_src, a, v, dtype, grad, ga, dv);
+    oracle_edge_softmax_backward(n_rows, row_ptr, heads, a, ga, gs);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        for (int h = 0; h < heads; ++h) {
+            for (int d = 0; d < head_dim; ++d) {
+                double gsum = 0.0;
+                for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e)
+                    gsum += gs[e * heads + h] *
+                            load_feat(k, dtype, ((int64_t)col_idx[e] * heads + h) * head_dim + d);
+                dq[(i * heads + h) * head_dim + d] = scale * gsum;
+            }
+        }
+    }
+    for (int64_t x = 0; x < n_src * heads * head_dim; ++x)
+        dk[x] = 0.0;
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < heads; ++h) {
+        for (int64_t e = 0; e < n_edges; ++e) {
+            int64_t i = row_of[e], j = col_idx[e];
+            for (int d = 0; d < head_dim; ++d)
+                dk[(j * heads + h) * head_dim + d] +=
+                    scale * gs[e * heads + h] * load_feat(q, dtype, (i * heads + h) * head_dim + d);
+        }
+    }
+    free(row_of);
+    free(s);
+    free(a);
+    free(ga);
+    free(gs);
+    return 0;
 }

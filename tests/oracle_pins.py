@@ -266,10 +266,144 @@ def pin_layer_dense(orc):
                                        rtol=1e-11, atol=1e-12)
 
 
+# ------------------------------------------------------------------------------- backward
+def _fd_check(loss, x, grad, eps=1e-6, rtol=1e-6, atol=1e-8):
+    """Central differences of the scalar loss at x, coordinate by coordinate, against grad.
+    ``loss`` reads x afresh on every call; x is restored after each probe."""
+    flat, gflat = x.reshape(-1), grad.reshape(-1)
+    for c in range(flat.size):
+        old = flat[c]
+        flat[c] = old + eps
+        lp = loss()
+        flat[c] = old - eps
+        lm = loss()
+        flat[c] = old
+        fd = (lp - lm) / (2 * eps)
+        assert abs(fd - gflat[c]) <= atol + rtol * abs(fd), f"coordinate {c}: finite difference {fd}, grad {gflat[c]}"
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient against central differences of the forward oracle (duplicates, zero rows,
+    sources no edge reads), with L = sum(output * G) for a random G."""
+    g = _graph(31, n=8, ns=7, max_deg=5, dup=True)
+    H, D = 2, 3
+    r = _rng(31)
+    s = r.standard_normal((g.n_edges, H))
+    w = r.standard_normal((g.n_edges, H))
+    X = r.standard_normal((g.n_src, H, D))
+    Q = r.standard_normal((g.n_rows, H, D))
+    K = r.standard_normal((g.n_src, H, D))
+    Ga = r.standard_normal((g.n_edges, H))
+    Go = r.standard_normal((g.n_rows, H, D))
+    rp, ci = g.row_ptr, g.col_idx
+    # softmax
+    a = orc.edge_softmax(rp, s)
+    _fd_check(lambda: float((orc.edge_softmax(rp, s) * Ga).sum()), s, orc.edge_softmax_backward(rp, a, Ga))
+    # aggregation
+    dw, dX = orc.aggregate_backward(rp, ci, w, X, Go)
+    _fd_check(lambda: float((orc.aggregate(rp, ci, w, X) * Go).sum()), w, dw)
+    _fd_check(lambda: float((orc.aggregate(rp, ci, w, X) * Go).sum()), X, dX)
+    # softmax + aggregation
+    ds, dX2 = orc.softmax_aggregate_backward(rp, ci, s, X, Go)
+    _fd_check(lambda: float((orc.softmax_aggregate(rp, ci, s, X) * Go).sum()), s, ds)
+    _fd_check(lambda: float((orc.softmax_aggregate(rp, ci, s, X) * Go).sum()), X, dX2)
+    # full layer
+    dq, dk, dv = orc.layer_backward(rp, ci, Q, K, X, Go, scale=0.7)
+    f = lambda: float((orc.layer(rp, ci, Q, K, X, scale=0.7) * Go).sum())
+    _fd_check(f, Q, dq)
+    _fd_check(f, K, dk)
+    _fd_check(f, X, dv)
+
+
+def _dense_layer_autograd(g, Q, K, V, Go, scale):
+    """torch autograd (fp64, CPU) of dense per-head attention over each row's edge multiset:
+    A[i,j] = C[i,j] exp(S[i,j] - m_i) / sum_j C[i,j] exp(S[i,j] - m_i), S = scale Q K^T, where C
+    counts the edges i -> j; rows without edges give 0."""
+    import torch
+    C = torch.from_numpy(_multiplicity(g))
+    has = (C > 0).any(1, keepdim=True)
+    Qt, Kt, Vt = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (Q, K, V))
+    loss = torch.zeros((), dtype=torch.float64)
+    for h in range(Q.shape[1]):
+        S = scale * (Qt[:, h, :] @ Kt[:, h, :].T)
+        m = torch.where(C > 0, S, torch.full_like(S, -torch.inf)).max(1, keepdim=True).values.detach()
+        m = torch.where(has, m, torch.zeros_like(m))
+        Ew = C * torch.exp(torch.where(C > 0, S - m, torch.zeros_like(S)))
+        A = Ew / torch.where(has, Ew.sum(1, keepdim=True), torch.ones_like(m))
+        loss = loss + ((A @ Vt[:, h, :]) * torch.from_numpy(Go[:, h, :])).sum()
+    loss.backward()
+    return Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy()
+
+
+def pin_layer_backward_autograd(orc):
+    """Full-layer gradients against torch autograd of the dense attention over edge multisets."""
+    for seed, (H, D), scale in [(32, (2, 4), 0.5), (33, (4, 8), 1.0)]:
+        g = _graph(seed, n=10, ns=12, max_deg=8, dup=True)
+        r = _rng(seed)
+        Q, K, V = (r.standard_normal(shape) for shape in
+                   ((g.n_rows, H, D), (g.n_src, H, D), (g.n_src, H, D)))
+        Go = r.standard_normal((g.n_rows, H, D))
+        dq, dk, dv = orc.layer_backward(g.row_ptr, g.col_idx, Q, K, V, Go, scale=scale)
+        tq, tk, tv = _dense_layer_autograd(g, Q, K, V, Go, scale)
+        np.testing.assert_allclose(dq, tq, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, tk, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, tv, rtol=1e-10, atol=1e-12)
+
+
+def pin_backward_invariants(orc):
+    """Softmax backward rows sum to zero and vanish for degree-1 rows and for a per-row constant
+    upstream gradient; zero rows give dq = +0.0; sources no edge reads give dk = dv = +0.0."""
+    g = _graph(34, n=15, ns=40, max_deg=6, dup=True, zero_frac=0.3)
+    H, D = 3, 4
+    r = _rng(34)
+    s = r.standard_normal((g.n_edges, H)) * 2
+    a = orc.edge_softmax(g.row_ptr, s)
+    Ga = r.standard_normal((g.n_edges, H))
+    ds = orc.edge_softmax_backward(g.row_ptr, a, Ga)
+    deg = g.degrees()
+    for i in range(g.n_rows):
+        b, e = g.row_ptr[i], g.row_ptr[i + 1]
+        if e > b:
+            np.testing.assert_allclose(ds[b:e].sum(0), 0.0, atol=1e-14 * (1 + np.abs(ds[b:e]).sum()))
+        if deg[i] == 1:
+            assert np.all(ds[b] == 0.0)
+    const = np.repeat(r.standard_normal((g.n_rows, H)), deg, axis=0)   # one value per (row, head)
+    dc = orc.edge_softmax_backward(g.row_ptr, a, const)
+    assert np.all(np.abs(dc) <= 1e-14 * (1 + np.abs(const)))
+    Q, K, V = (r.standard_normal(shape) for shape in ((g.n_rows, H, D), (g.n_src, H, D), (g.n_src, H, D)))
+    Go = r.standard_normal((g.n_rows, H, D))
+    dq, dk, dv = orc.layer_backward(g.row_ptr, g.col_idx, Q, K, V, Go, scale=0.5)
+    zr = deg == 0
+    unread = np.bincount(g.col_idx, minlength=g.n_src) == 0
+    assert zr.any() and unread.any()
+    for arr, sel in ((dq, zr), (dk, unread), (dv, unread)):
+        assert np.all(arr[sel] == 0.0) and not np.any(np.signbit(arr[sel]))
+
+
+def pin_aggregate_backward_integer_exact(orc):
+    """Integer weights, features and upstream gradients: both gradients are exact integer sums,
+    equal bitwise to int64 dense products (dW_dense = G X^T sampled at the edges, dX = W_dense^T G)."""
+    g = _graph(35, n=13, ns=9, max_deg=7, dup=True)
+    H, D = 2, 16
+    r = _rng(35)
+    w = r.integers(-4, 5, (g.n_edges, H)).astype(np.float64)
+    X = r.integers(-8, 9, (g.n_src, H, D)).astype(np.float32)
+    Go = r.integers(-8, 9, (g.n_rows, H, D)).astype(np.float64)
+    dw, dX = orc.aggregate_backward(g.row_ptr, g.col_idx, w, G.f32_to_bf16_bits(X), Go)
+    rows = G.row_of_edge(g.row_ptr)
+    Xi, Gi, wi = X.astype(np.int64), Go.astype(np.int64), w.astype(np.int64)
+    for h in range(H):
+        assert np.array_equal(dw[:, h], (Gi[:, h, :] @ Xi[:, h, :].T)[rows, g.col_idx].astype(np.float64))
+        Wd = np.zeros((g.n_rows, g.n_src), np.int64)
+        np.add.at(Wd, (rows, g.col_idx), wi[:, h])
+        assert np.array_equal(dX[:, h, :], (Wd.T @ Gi[:, h, :]).astype(np.float64))
+
+
 ALL_PINS = [pin_sddmm_dense, pin_sddmm_integer_exact, pin_softmax_closed_forms, pin_softmax_dense,
             pin_softmax_invariants, pin_aggregate_dense, pin_aggregate_integer_exact,
             pin_zero_rows_positive_zero, pin_softmax_aggregate_dense, pin_softmax_aggregate_closed_forms,
-            pin_layer_dense]
+            pin_layer_dense, pin_backward_finite_differences, pin_layer_backward_autograd,
+            pin_backward_invariants, pin_aggregate_backward_integer_exact]
 
 
 def run_all(orc) -> list:

@@ -35,8 +35,9 @@ MUTANTS = [
     ("softmax_not_normalised", "exp(scores[e * heads + h] - m) / z;", "exp(scores[e * heads + h] - m);"),
     ("softmax_end_off_by_one", "for (int64_t e = start; e < end; ++e)\n                z +=",
      "for (int64_t e = start; e + 1 < end; ++e)\n                z +="),
-    ("aggregate_head_dropped_in_gather", "((int64_t)col_idx[e] * heads + h) * head_dim + d",
-     "((int64_t)col_idx[e] * heads) * head_dim + d"),
+    ("aggregate_head_dropped_in_gather",
+     "acc += weights[e * heads + h] *\n                           load_feat(feat, dtype, ((int64_t)col_idx[e] * heads + h)",
+     "acc += weights[e * heads + h] *\n                           load_feat(feat, dtype, ((int64_t)col_idx[e] * heads)"),
     ("aggregate_weight_head0", "acc += weights[e * heads + h] *", "acc += weights[e * heads] *"),
     ("aggregate_end_off_by_one", "for (int64_t e = start; e < end; ++e)\n                    acc +=",
      "for (int64_t e = start; e + 1 < end; ++e)\n                    acc +="),
@@ -50,6 +51,22 @@ MUTANTS = [
     ("bf16_decode_shift", "<< 16;", "<< 15;"),
     ("layer_query_row_wrong", "dst[e] = (int32_t)i;", "dst[e] = 0;"),
     ("layer_k_v_swapped", "scores, v, dtype, out);", "scores, k, dtype, out);"),
+    # backward
+    ("softmax_bwd_dot_dropped", "out[e * heads + h] = alpha[e * heads + h] * (grad[e * heads + h] - dot);",
+     "out[e * heads + h] = alpha[e * heads + h] * grad[e * heads + h];"),
+    ("softmax_bwd_sign", "out[e * heads + h] = alpha[e * heads + h] * (grad[e * heads + h] - dot);",
+     "out[e * heads + h] = alpha[e * heads + h] * (grad[e * heads + h] + dot);"),
+    ("agg_bwd_dweights_head0", "acc += grad[(i * heads + h) * head_dim + d] *\n                           load_feat(feat",
+     "acc += grad[(i * heads) * head_dim + d] *\n                           load_feat(feat"),
+    ("agg_bwd_dfeat_wrong_column", "int64_t j = col_idx[e];\n                for (int d = 0; d < head_dim; ++d)\n                    dfeat",
+     "int64_t j = col_idx[row_ptr[i]];\n                for (int d = 0; d < head_dim; ++d)\n                    dfeat"),
+    ("layer_bwd_dq_scale_dropped", "dq[(i * heads + h) * head_dim + d] = scale * gsum;",
+     "dq[(i * heads + h) * head_dim + d] = gsum;"),
+    ("layer_bwd_dk_reads_k", "scale * gs[e * heads + h] * load_feat(q, dtype, (i * heads + h) * head_dim + d);",
+     "scale * gs[e * heads + h] * load_feat(k, dtype, (j * heads + h) * head_dim + d);"),
+    ("layer_bwd_dv_weights_are_scores", "n_src, a, v, dtype, grad, ga, dv);", "n_src, s, v, dtype, grad, ga, dv);"),
+    ("softagg_bwd_weights_are_scores", "n_src, alpha, feat, dtype, grad, ga, dfeat);",
+     "n_src, scores, feat, dtype, grad, ga, dfeat);"),
 ]
 
 
