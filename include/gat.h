@@ -180,6 +180,103 @@ int gat_shape_supported(int heads, int head_dim);
 /* sizeof(gat_plan) as compiled into the library, for bindings that mirror the struct (host). */
 size_t gat_plan_sizeof(void);
 
+/* ------------------------------------------------------------------------------------------
+ * Backward.  No page writes the backward pass out; the l1_p10 page (edge-only SDDMM, the
+ * passage on the backward pass) notes that gradients sum into the feature rows that edges read.
+ * Each entry point below computes the derivative of a forward entry point above, given
+ * grad_out = dL/d(forward output).  Gradients with respect to gathered tables (feat, k, v) are
+ * aggregations over the transposed graph (a gat_csc), so every sum runs in a fixed order and no
+ * atomic additions are used.
+ * ------------------------------------------------------------------------------------------ */
+
+/*
+ * Transposed view of a CSR graph, built on the device by gat_csc_build and owned by the caller
+ * (its arrays live in the caller's workspace `ws`; the struct only records offsets):
+ *   col_ptr  int32 [n_src+1]    entries of source j are [col_ptr[j], col_ptr[j+1])
+ *   row_idx  int32 [n_edges]    destination row of each entry
+ *   perm     int32 [n_edges]    CSR edge id of each entry; entries of one source are in
+ *                               increasing edge id (a stable sort of the edges by column)
+ *   rows     int32 [n_edges]    destination row of each CSR edge (CSR order)
+ *   stage    fp32  [n_edges*heads]  per-edge values moved into CSC order during a call
+ *   plan     a degree-binning plan of the transposed graph (rows = sources)
+ * Calls that use one gat_csc write its stage, so they must be ordered on one stream.
+ */
+typedef struct gat_csc {
+    int64_t n_rows, n_src, n_edges;
+    int32_t heads, head_dim;
+    void* ws;
+    size_t ws_bytes;
+    size_t off_col_ptr, off_row_idx, off_perm, off_rows, off_stage;   /* byte offsets into ws */
+    gat_plan plan;
+    uint32_t magic;
+} gat_csc;
+
+/* Workspace bytes for gat_csc_build (0 if the sizes or shape are unsupported). */
+size_t gat_csc_workspace_bytes(int64_t n_rows, int64_t n_src, int64_t n_edges, int heads, int head_dim);
+
+/* Size of gat_csc as compiled into the library (for bindings that mirror the struct). */
+size_t gat_csc_sizeof(void);
+
+/*
+ * Builds the transposed view of (row_ptr, col_idx) into ws (device memory of at least
+ * gat_csc_workspace_bytes, 256-byte aligned) and fills *csc.  heads/head_dim size the stage
+ * and the plan's partial states for the calls that will use it.  Enqueued on `stream`; no
+ * synchronisation.  Requires 0 <= col_idx[e] < n_src (not checked on the device).
+ */
+gat_status gat_csc_build(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                         int64_t n_edges, int heads, int head_dim, void* ws, size_t ws_bytes,
+                         gat_csc* csc, hipStream_t stream);
+
+/*
+ * Edge softmax backward (derivative of gat_edge_softmax): with alpha its output and grad =
+ * dL/dalpha, both fp32 [n_edges,heads],
+ *   out[e,h] = alpha[e,h] * (grad[e,h] - sum_{e' in row i} alpha[e',h] * grad[e',h])
+ * out may equal grad (in place).  plan: NULL or a plan built for this row_ptr.
+ */
+gat_status gat_edge_softmax_backward(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, int heads,
+                                     const float* alpha, const float* grad, float* out,
+                                     const gat_plan* plan, hipStream_t stream);
+
+/*
+ * Aggregation backward (derivative of gat_aggregate), grad_out fp32 [n_rows,heads,head_dim]:
+ *   dweights[e,h] = <grad_out[i,h,:], feat[col_idx[e],h,:]>                 (e in row i)
+ *   dfeat[j,h,:]  = sum over the edges e with col_idx[e] = j of weights[e,h] * grad_out[i,h,:]
+ * dweights fp32 [n_edges,heads] and dfeat fp32 [n_src,heads,head_dim] may each be NULL (not
+ * computed); dfeat is +0.0 for sources no edge reads.  csc: built for this graph with the same
+ * heads and head_dim (required: it supplies the row of each edge, and the transposed graph).
+ */
+gat_status gat_aggregate_backward(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows,
+                                  int64_t n_src, int64_t n_edges, const float* weights, const void* feat,
+                                  gat_dtype dtype, int heads, int head_dim, const float* grad_out,
+                                  float* dweights, float* dfeat, const gat_csc* csc, hipStream_t stream);
+
+/* Workspace bytes for gat_fused_layer_backward (0 if the sizes are unsupported). */
+size_t gat_layer_backward_workspace_bytes(int64_t n_edges, int heads);
+
+/*
+ * Fused attention backward (derivative of gat_fused_layer), grad_out fp32
+ * [n_rows,heads,head_dim].  With s the scores, alpha = edge_softmax(s) and
+ * g[e,h] = <grad_out[i,h,:], v[col_idx[e],h,:]> (= dL/dalpha):
+ *   g_s[e,h] = alpha[e,h] * (g[e,h] - sum_{e' in row i} alpha[e',h] * g[e',h])
+ *   dv[j]    = sum over the edges e with col_idx[e] = j of alpha[e] * grad_out[i]
+ * Modes as in the forward (exactly one of scores or (q, k) when n_edges > 0):
+ *  - scores given: dscores = g_s (fp32 [n_edges,heads]); dq, dk unused (may be NULL).
+ *  - q, k given (s = scale * <q_i, k_j>, recomputed here): dq[i] = scale * sum_{e in row i}
+ *    g_s[e] * k[col_idx[e]], dk[j] = scale * sum over the edges e with col_idx[e] = j of
+ *    g_s[e] * q[i] (fp32 [n_rows|n_src,heads,head_dim]); dscores unused (may be NULL).
+ * dv is always computed; dv, dk are +0.0 for sources no edge reads, dq for rows without edges.
+ * plan: built for this row_ptr (required); csc: built for this graph with the same heads and
+ * head_dim (required).  ws: device workspace of at least gat_layer_backward_workspace_bytes
+ * (scores, alpha, g), 256-byte aligned.  Calls sharing ws, plan or csc must be ordered.
+ */
+gat_status gat_fused_layer_backward(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows,
+                                    int64_t n_src, int64_t n_edges, int heads, int head_dim, gat_dtype dtype,
+                                    const float* scores, const void* q, const void* k, float scale,
+                                    const void* v, const float* grad_out,
+                                    float* dscores, float* dq, float* dk, float* dv,
+                                    const gat_plan* plan, const gat_csc* csc, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,6 +124,108 @@ gat_status check_plan(const gat_plan* p, int64_t n_rows, int64_t n_edges, int64_
 
 gat_status hip_status(hipError_t e) { return e == hipSuccess ? GAT_OK : GAT_ERR_HIP; }
 
+// Fills *p for a plan of layout L in ws and enqueues its build on row_ptr.
+hipError_t build_plan(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, int heads, int head_dim,
+                      int short_max, int seg_len, const Layout& L, void* ws, size_t ws_bytes, gat_plan* p,
+                      hipStream_t stream) {
+    memset(p, 0, sizeof *p);
+    p->n_rows = n_rows;
+    p->n_edges = n_edges;
+    p->short_max = short_max;
+    p->seg_len = seg_len;
+    p->heads = heads;
+    p->head_dim = head_dim;
+    p->state_floats = L.state_floats;
+    p->seg_capacity = L.seg_cap;
+    p->hub_capacity = L.hub_cap;
+    p->hubseg_capacity = L.hubseg_cap;
+    p->n_blocks = L.n_blocks;
+    p->ws = ws;
+    p->ws_bytes = ws_bytes;
+    p->off_counts = L.off_counts;
+    p->off_blocks = L.off_blocks;
+    p->off_segs = L.off_segs;
+    p->off_hubs = L.off_hubs;
+    p->off_partials = L.off_partials;
+    p->magic = kPlanMagic;
+    char* base = static_cast<char*>(ws);
+    return gat::launch_plan(row_ptr, n_rows, short_max, seg_len, reinterpret_cast<int4*>(base + L.off_blocks),
+                            L.n_blocks, reinterpret_cast<int32_t*>(base + L.off_counts),
+                            reinterpret_cast<int4*>(base + L.off_segs), reinterpret_cast<int4*>(base + L.off_hubs),
+                            stream);
+}
+
+// ------------------------------------------------------------------------------ transposed view
+constexpr uint32_t kCscMagic = 0x47415443u;   // "GATC"
+
+struct CscLayout {
+    int sort_passes;
+    size_t off_col_ptr, off_row_idx, off_rows, off_keys[2], off_vals[2], off_hist, off_sums, off_stage, off_plan;
+    Layout plan;
+    size_t total;
+};
+
+CscLayout csc_layout(int64_t n_rows, int64_t n_src, int64_t n_edges, int heads, int head_dim) {
+    (void)n_rows;
+    CscLayout C{};
+    int bits = 0;
+    while (bits < 31 && ((int64_t)1 << bits) < n_src) ++bits;   // columns are < n_src
+    C.sort_passes = (bits + gat::kRadixDigitBits - 1) / gat::kRadixDigitBits;
+    if (C.sort_passes < 1) C.sort_passes = 1;
+    const int64_t hist = (int64_t)gat::kRadixDigits * gat::radix_tiles(n_edges);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    C.off_col_ptr = take((size_t)(n_src + 1) * 4);
+    C.off_row_idx = take((size_t)n_edges * 4);
+    C.off_rows = take((size_t)n_edges * 4);
+    for (int b = 0; b < 2; ++b) {
+        C.off_keys[b] = take((size_t)n_edges * 4);
+        C.off_vals[b] = take((size_t)n_edges * 4);
+    }
+    C.off_hist = take((size_t)hist * 4);
+    C.off_sums = take((size_t)(gat::scan_tiles(hist) + 1) * 4);
+    C.off_stage = take((size_t)n_edges * heads * 4);
+    C.plan = plan_layout(n_src, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN);
+    C.off_plan = take(C.plan.total);
+    C.total = off;
+    return C;
+}
+
+// A gat_csc usable for a call on this graph with this shape.
+gat_status check_csc(const gat_csc* c, int64_t n_rows, int64_t n_src, int64_t n_edges, int heads, int head_dim) {
+    if (c->magic != kCscMagic || c->ws == nullptr) return GAT_ERR_ARGS;
+    if (c->n_rows != n_rows || c->n_src != n_src || c->n_edges != n_edges) return GAT_ERR_WORKSPACE;
+    if (c->heads != heads || c->head_dim != head_dim) return GAT_ERR_WORKSPACE;
+    return GAT_OK;
+}
+
+template <typename T>
+T* at(const gat_csc* c, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(c->ws) + off);
+}
+
+// Layer-backward workspace: scores, alpha and the edge gradient, each [E,H] fp32.
+struct BwdLayout {
+    size_t off_scores, off_alpha, off_grad, total;
+};
+
+BwdLayout bwd_layout(int64_t n_edges, int heads) {
+    BwdLayout B{};
+    size_t off = 0;
+    B.off_scores = off;
+    off = align_up(off + (size_t)n_edges * heads * 4);
+    B.off_alpha = off;
+    off = align_up(off + (size_t)n_edges * heads * 4);
+    B.off_grad = off;
+    off = align_up(off + (size_t)n_edges * heads * 4);
+    B.total = off > kAlign ? off : kAlign;   // never 0: 0 reports unsupported sizes
+    return B;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,32 +265,8 @@ gat_status gat_plan_build(const int32_t* row_ptr, int64_t n_rows, int64_t n_edge
     const Layout L = plan_layout(n_rows, n_edges, heads, head_dim, short_max, seg_len);
     if (ws_bytes < L.total) return GAT_ERR_WORKSPACE;
     gat_plan p;
-    memset(&p, 0, sizeof p);
-    p.n_rows = n_rows;
-    p.n_edges = n_edges;
-    p.short_max = short_max;
-    p.seg_len = seg_len;
-    p.heads = heads;
-    p.head_dim = head_dim;
-    p.state_floats = L.state_floats;
-    p.seg_capacity = L.seg_cap;
-    p.hub_capacity = L.hub_cap;
-    p.hubseg_capacity = L.hubseg_cap;
-    p.n_blocks = L.n_blocks;
-    p.ws = ws;
-    p.ws_bytes = ws_bytes;
-    p.off_counts = L.off_counts;
-    p.off_blocks = L.off_blocks;
-    p.off_segs = L.off_segs;
-    p.off_hubs = L.off_hubs;
-    p.off_partials = L.off_partials;
-    p.magic = kPlanMagic;
-    char* base = static_cast<char*>(ws);
-    const hipError_t e = gat::launch_plan(row_ptr, n_rows, short_max, seg_len,
-                                          reinterpret_cast<int4*>(base + L.off_blocks), L.n_blocks,
-                                          reinterpret_cast<int32_t*>(base + L.off_counts),
-                                          reinterpret_cast<int4*>(base + L.off_segs),
-                                          reinterpret_cast<int4*>(base + L.off_hubs), stream);
+    const hipError_t e = build_plan(row_ptr, n_rows, n_edges, heads, head_dim, short_max, seg_len, L, ws, ws_bytes,
+                                    &p, stream);
     if (e != hipSuccess) return GAT_ERR_HIP;
     *plan = p;
     return GAT_OK;
@@ -263,6 +341,178 @@ gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64
     const int mode = have_scores ? gat::kSoftAgg : gat::kLayer;
     return hip_status(gat::launch_spmm(mode, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, scores, q, k, v,
                                        scale, out, plan ? &pv : nullptr, stream));
+}
+
+// ------------------------------------------------------------------------------ backward
+size_t gat_csc_sizeof(void) { return sizeof(gat_csc); }
+
+size_t gat_csc_workspace_bytes(int64_t n_rows, int64_t n_src, int64_t n_edges, int heads, int head_dim) {
+    if (!size_ok(n_rows) || !size_ok(n_src) || !edges_ok(n_edges) || !shape_ok(heads, head_dim)) return 0;
+    return csc_layout(n_rows, n_src, n_edges, heads, head_dim).total;
+}
+
+gat_status gat_csc_build(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                         int64_t n_edges, int heads, int head_dim, void* ws, size_t ws_bytes, gat_csc* csc,
+                         hipStream_t stream) {
+    if (csc == nullptr || ws == nullptr || row_ptr == nullptr) return GAT_ERR_NULL;
+    if (!size_ok(n_rows) || !size_ok(n_src) || !edges_ok(n_edges)) return GAT_ERR_SIZE;
+    if (!shape_ok(heads, head_dim)) return GAT_ERR_UNSUPPORTED;
+    if (n_edges > 0 && (col_idx == nullptr || n_src == 0 || n_rows == 0)) return n_src == 0 || n_rows == 0 ? GAT_ERR_ARGS : GAT_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return GAT_ERR_ARGS;
+    const CscLayout C = csc_layout(n_rows, n_src, n_edges, heads, head_dim);
+    if (ws_bytes < C.total) return GAT_ERR_WORKSPACE;
+    gat_csc c;
+    memset(&c, 0, sizeof c);
+    c.n_rows = n_rows;
+    c.n_src = n_src;
+    c.n_edges = n_edges;
+    c.heads = heads;
+    c.head_dim = head_dim;
+    c.ws = ws;
+    c.ws_bytes = ws_bytes;
+    c.off_col_ptr = C.off_col_ptr;
+    c.off_row_idx = C.off_row_idx;
+    c.off_rows = C.off_rows;
+    c.off_stage = C.off_stage;
+    c.off_perm = C.off_vals[(C.sort_passes - 1) % 2];
+    char* base = static_cast<char*>(ws);
+    auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+    hipError_t e = gat::launch_expand_rows(row_ptr, n_rows, I(C.off_rows), stream);
+    // stable LSD passes over the column bits: (column, edge id) ends sorted by column, then edge id
+    for (int pass = 0; e == hipSuccess && pass < C.sort_passes; ++pass) {
+        const int32_t* kin = pass == 0 ? col_idx : I(C.off_keys[(pass - 1) % 2]);
+        const int32_t* vin = pass == 0 ? nullptr : I(C.off_vals[(pass - 1) % 2]);
+        e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), n_edges,
+                                   pass * gat::kRadixDigitBits, I(C.off_hist), I(C.off_sums), stream);
+    }
+    if (e == hipSuccess)
+        e = gat::launch_csc_finish(I(C.off_keys[(C.sort_passes - 1) % 2]), I(c.off_perm), I(C.off_rows), n_edges,
+                                   n_src, I(C.off_col_ptr), I(C.off_row_idx), stream);
+    if (e == hipSuccess)
+        e = build_plan(I(C.off_col_ptr), n_src, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN,
+                       C.plan, base + C.off_plan, C.plan.total, &c.plan, stream);
+    if (e != hipSuccess) return GAT_ERR_HIP;
+    c.magic = kCscMagic;
+    *csc = c;
+    return GAT_OK;
+}
+
+gat_status gat_edge_softmax_backward(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, int heads,
+                                     const float* alpha, const float* grad, float* out, const gat_plan* plan,
+                                     hipStream_t stream) {
+    if (!size_ok(n_rows) || !edges_ok(n_edges)) return GAT_ERR_SIZE;
+    if (!heads_ok(heads)) return GAT_ERR_UNSUPPORTED;
+    if (n_rows == 0 || n_edges == 0) return GAT_OK;
+    if (!row_ptr || !alpha || !grad || !out) return GAT_ERR_NULL;
+    gat::PlanView pv;
+    if (plan) {
+        const gat_status st = check_plan(plan, n_rows, n_edges, heads);
+        if (st != GAT_OK) return st;
+        pv = plan_view(plan);
+    }
+    return hip_status(
+        gat::launch_softmax_backward(heads, row_ptr, n_rows, alpha, grad, out, 1.f, plan ? &pv : nullptr, stream));
+}
+
+gat_status gat_aggregate_backward(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                                  int64_t n_edges, const float* weights, const void* feat, gat_dtype dtype, int heads,
+                                  int head_dim, const float* grad_out, float* dweights, float* dfeat,
+                                  const gat_csc* csc, hipStream_t stream) {
+    if (!size_ok(n_rows) || !size_ok(n_src) || !edges_ok(n_edges)) return GAT_ERR_SIZE;
+    if (!shape_ok(heads, head_dim) || !dtype_ok(dtype)) return GAT_ERR_UNSUPPORTED;
+    if (csc == nullptr) return GAT_ERR_NULL;
+    const gat_status st = check_csc(csc, n_rows, n_src, n_edges, heads, head_dim);
+    if (st != GAT_OK) return st;
+    if (n_edges > 0 && (!row_ptr || !col_idx || !grad_out)) return GAT_ERR_NULL;
+    if (n_edges > 0 && dweights && !feat) return GAT_ERR_NULL;
+    if (n_edges > 0 && dfeat && !weights) return GAT_ERR_NULL;
+    hipError_t e = hipSuccess;
+    if (dweights && n_edges > 0)
+        e = gat::launch_edge_dot(dtype, heads, head_dim, at<int32_t>(csc, csc->off_rows), col_idx, n_edges, grad_out,
+                                 feat, dweights, stream);
+    if (e == hipSuccess && dfeat && n_src > 0) {
+        const int32_t* perm = at<int32_t>(csc, csc->off_perm);
+        float* stage = at<float>(csc, csc->off_stage);
+        e = gat::launch_permute_edges(heads, perm, weights, n_edges, stage, stream);
+        const gat::PlanView pv = plan_view(&csc->plan);
+        if (e == hipSuccess)
+            e = gat::launch_spmm(gat::kAgg, GAT_F32, heads, head_dim, at<int32_t>(csc, csc->off_col_ptr),
+                                 at<int32_t>(csc, csc->off_row_idx), n_src, n_rows, stage, nullptr, nullptr, grad_out,
+                                 1.f, dfeat, &pv, stream);
+    }
+    return hip_status(e);
+}
+
+size_t gat_layer_backward_workspace_bytes(int64_t n_edges, int heads) {
+    if (!edges_ok(n_edges) || !heads_ok(heads)) return 0;
+    return bwd_layout(n_edges, heads).total;
+}
+
+gat_status gat_fused_layer_backward(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                                    int64_t n_edges, int heads, int head_dim, gat_dtype dtype, const float* scores,
+                                    const void* q, const void* k, float scale, const void* v, const float* grad_out,
+                                    float* dscores, float* dq, float* dk, float* dv, const gat_plan* plan,
+                                    const gat_csc* csc, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!size_ok(n_rows) || !size_ok(n_src) || !edges_ok(n_edges)) return GAT_ERR_SIZE;
+    if (!shape_ok(heads, head_dim) || !dtype_ok(dtype)) return GAT_ERR_UNSUPPORTED;
+    const bool have_scores = scores != nullptr;
+    const bool have_q = q != nullptr, have_k = k != nullptr;
+    if (n_edges > 0 && (have_q != have_k || have_scores == have_q)) return GAT_ERR_ARGS;
+    const bool layer = !have_scores && have_q;
+    if (plan == nullptr || csc == nullptr || ws == nullptr) return GAT_ERR_NULL;
+    gat_status st = check_plan(plan, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
+    if (st != GAT_OK) return st;
+    st = check_csc(csc, n_rows, n_src, n_edges, heads, head_dim);
+    if (st != GAT_OK) return st;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return GAT_ERR_ARGS;
+    const BwdLayout B = bwd_layout(n_edges, heads);
+    if (ws_bytes < B.total) return GAT_ERR_WORKSPACE;
+    if (n_src > 0 && !dv) return GAT_ERR_NULL;
+    if (layer && ((n_rows > 0 && !dq) || (n_src > 0 && !dk))) return GAT_ERR_NULL;
+    if (n_edges > 0 && (!row_ptr || !col_idx || !v || !grad_out)) return GAT_ERR_NULL;
+    if (n_edges > 0 && !layer && !dscores) return GAT_ERR_NULL;
+    char* base = static_cast<char*>(ws);
+    float* s_ws = reinterpret_cast<float*>(base + B.off_scores);
+    float* alpha = reinterpret_cast<float*>(base + B.off_alpha);
+    float* g = reinterpret_cast<float*>(base + B.off_grad);
+    const int32_t* rows = at<int32_t>(csc, csc->off_rows);
+    const int32_t* perm = at<int32_t>(csc, csc->off_perm);
+    const int32_t* col_ptr = at<int32_t>(csc, csc->off_col_ptr);
+    const int32_t* row_idx = at<int32_t>(csc, csc->off_row_idx);
+    float* stage = at<float>(csc, csc->off_stage);
+    const gat::PlanView pv = plan_view(plan);
+    const gat::PlanView cv = plan_view(&csc->plan);
+    hipError_t e = hipSuccess;
+    if (n_edges > 0) {
+        const float* s = scores;
+        if (layer) {   // the forward's scores, recomputed once
+            e = gat::launch_sddmm(dtype, heads, head_dim, col_idx, rows, n_edges, k, n_src, q, n_rows, scale, s_ws,
+                                  stream);
+            s = s_ws;
+        }
+        // alpha, then dL/dalpha[e] = <grad_out[i], v[j]>, then the softmax backward (scaled for q, k)
+        if (e == hipSuccess) e = gat::launch_softmax(heads, row_ptr, n_rows, s, alpha, &pv, stream);
+        if (e == hipSuccess)
+            e = gat::launch_edge_dot(dtype, heads, head_dim, rows, col_idx, n_edges, grad_out, v, g, stream);
+        if (e == hipSuccess)
+            e = gat::launch_softmax_backward(heads, row_ptr, n_rows, alpha, g, layer ? g : dscores,
+                                             layer ? scale : 1.f, &pv, stream);
+        if (e == hipSuccess) e = gat::launch_permute_edges(heads, perm, alpha, n_edges, stage, stream);
+    }
+    // dv over the transposed graph (+0.0 for sources no edge reads)
+    if (e == hipSuccess && n_src > 0)
+        e = gat::launch_spmm(gat::kAgg, GAT_F32, heads, head_dim, col_ptr, row_idx, n_src, n_rows, stage, nullptr,
+                             nullptr, grad_out, 1.f, dv, &cv, stream);
+    if (layer) {
+        if (e == hipSuccess && n_rows > 0)
+            e = gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, g, nullptr,
+                                 nullptr, k, 1.f, dq, &pv, stream);
+        if (e == hipSuccess && n_edges > 0) e = gat::launch_permute_edges(heads, perm, g, n_edges, stage, stream);
+        if (e == hipSuccess && n_src > 0)
+            e = gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, col_ptr, row_idx, n_src, n_rows, stage, nullptr,
+                                 nullptr, q, 1.f, dk, &cv, stream);
+    }
+    return hip_status(e);
 }
 
 }  // extern "C"

@@ -1,0 +1,509 @@
+// Backward of the path, and the transposed (CSC) view of the graph that it needs.
+//
+// The forward steps are out[i] = sum over row i of w[e] * x[col[e]] and its softmax / SDDMM
+// relatives.  Their gradients with respect to the gathered tables sum over the edges that read
+// each source row.  The SDDMM page (POPCORNBENCH l1_p10, the passage on the backward pass) has
+// those sums done with atomic additions; here they are plain gathers over the transposed graph
+// (sources as rows), built once per graph by a stable sort of the edges by column, so the
+// transposed aggregation reuses the forward kernels and every sum has a fixed order.
+//
+// Kernels in this file:
+//  * expand_rows: row id of every CSR edge.
+//  * radix_hist / radix_scatter: one pass of an LSD radix sort (4-bit digits) of (column, edge
+//    id) pairs, stable, so the final order is by column and then by edge id; scan_*: the
+//    exclusive scan of the per-tile digit counts between the two.
+//  * csc_bounds: column pointers from the sorted columns; gather_rows: row id per CSC entry.
+//  * permute_edges: per-edge values [E,H] moved into CSC order.
+//  * edge_dot: per edge and head, <G[row(e)], F[col(e)]> with G fp32 and F fp32 or bf16 (the
+//    gradient of the aggregation weights, and of the softmax output in the fused backward).
+//  * softmax_bwd_*: out = scale * alpha * (g - sum_row alpha * g), by degree class like the
+//    forward.
+#include <math.h>
+
+#include "kernels.hpp"
+
+namespace gat {
+
+namespace {
+
+// ------------------------------------------------------------------------------ row ids
+// A wave per 64 rows: a row of up to 64 edges is written by its own lane, a longer one by the
+// whole wave.
+__global__ __launch_bounds__(kBlock) void expand_rows_kernel(const int32_t* __restrict__ row_ptr, int64_t n_rows,
+                                                             int32_t* __restrict__ rows) {
+    const int lane = lane_id();
+    const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * kWave;
+    if (r0 >= n_rows) return;
+    const int64_t r = r0 + lane;
+    int b = 0, e = 0;
+    if (r < n_rows) {
+        b = row_ptr[r];
+        e = row_ptr[r + 1];
+    }
+    if (e - b <= kWave)
+        for (int x = b; x < e; ++x) rows[x] = (int32_t)r;
+    uint64_t big = __ballot(r < n_rows && e - b > kWave);
+    while (big) {
+        const int l = __builtin_ctzll(big);
+        big &= big - 1;
+        const int bb = shfl(b, l), ee = shfl(e, l);
+        for (int x = bb + lane; x < ee; x += kWave) rows[x] = (int32_t)(r0 + l);
+    }
+}
+
+// ------------------------------------------------------------------------------ radix sort
+// A tile is kSortItems consecutive keys per thread: thread t owns items t*16 .. t*16+15 of the
+// tile, so a stable rank is (same-digit items of threads < t) + (same-digit items earlier in t).
+constexpr int kRadixBins = kRadixDigits;
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kBlock * kSortItems;
+
+__global__ __launch_bounds__(kBlock) void radix_hist_kernel(const int32_t* __restrict__ keys, int64_t n, int shift,
+                                                            int32_t* __restrict__ hist, int64_t n_tiles) {
+    __shared__ int cnt[kRadixBins];
+    const int t = threadIdx.x;
+    if (t < kRadixBins) cnt[t] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const int64_t i = base + (int64_t)k * kBlock + t;
+        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & (kRadixBins - 1)], 1);
+    }
+    __syncthreads();
+    if (t < kRadixBins) hist[(int64_t)t * n_tiles + blockIdx.x] = cnt[t];
+}
+
+// vin == nullptr: the values are the item positions (the first pass, identity order).
+__global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const int32_t* __restrict__ kin,
+                                                               const int32_t* __restrict__ vin,
+                                                               int32_t* __restrict__ kout, int32_t* __restrict__ vout,
+                                                               int64_t n, int shift, const int32_t* __restrict__ offs,
+                                                               int64_t n_tiles) {
+    __shared__ int cnt[kRadixBins][kBlock];       // per digit, per thread: count, then rank base
+    __shared__ int chunk[kRadixBins][kBlock / 16];
+    const int t = threadIdx.x;
+    const int64_t i0 = (int64_t)blockIdx.x * kSortTile + (int64_t)t * kSortItems;
+    int key[kSortItems];
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) key[k] = i0 + k < n ? kin[i0 + k] : 0;
+#pragma unroll
+    for (int d = 0; d < kRadixBins; ++d) cnt[d][t] = 0;
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k)
+        if (i0 + k < n) cnt[(key[k] >> shift) & (kRadixBins - 1)][t] += 1;
+    __syncthreads();
+    // exclusive scan of cnt[d][0..255] for every digit: 16 threads per digit scan 16 entries each,
+    // then one thread per digit scans the 16 chunk sums
+    {
+        const int d = t / 16, ch = t % 16;
+        int s = 0;
+        for (int j = 0; j < 16; ++j) {
+            const int v = cnt[d][ch * 16 + j];
+            cnt[d][ch * 16 + j] = s;
+            s += v;
+        }
+        chunk[d][ch] = s;
+    }
+    __syncthreads();
+    if (t < kRadixBins) {
+        int s = 0;
+        for (int ch = 0; ch < 16; ++ch) {
+            const int v = chunk[t][ch];
+            chunk[t][ch] = s;
+            s += v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        if (i0 + k < n) {
+            const int d = (key[k] >> shift) & (kRadixBins - 1);
+            const int64_t pos = (int64_t)offs[(int64_t)d * n_tiles + blockIdx.x] + chunk[d][t / 16] + cnt[d][t];
+            cnt[d][t] += 1;   // only this thread touches column t
+            kout[pos] = key[k];
+            vout[pos] = vin ? vin[i0 + k] : (int32_t)(i0 + k);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ exclusive scan
+// out[i] = sum of in[0..i) for n int32 values (totals below 2^31); out may alias in.
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kBlock * kScanItems;
+
+__device__ int block_exscan_int(int v, int& total) {
+    __shared__ int wsum[kWavesPerBlock];
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+    }
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    int off = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        if (i < w) off += wsum[i];
+        total += wsum[i];
+    }
+    __syncthreads();
+    return off + inc - v;
+}
+
+__global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const int32_t* __restrict__ in, int64_t n,
+                                                             int32_t* __restrict__ sums) {
+    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k)
+        if (i0 + k < n) s += in[i0 + k];
+    int total;
+    block_exscan_int(s, total);
+    if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+
+// one workgroup: exclusive scan of the tile sums, in place
+__global__ __launch_bounds__(kBlock) void scan_sums_kernel(int32_t* __restrict__ sums, int64_t n) {
+    int carry = 0;
+    for (int64_t base = 0; base < n; base += kBlock) {
+        const int64_t i = base + threadIdx.x;
+        const int v = i < n ? sums[i] : 0;
+        int total;
+        const int ex = block_exscan_int(v, total);
+        if (i < n) sums[i] = carry + ex;
+        carry += total;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void scan_apply_kernel(const int32_t* in, int64_t n,
+                                                            const int32_t* __restrict__ sums, int32_t* out) {
+    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    int v[kScanItems];
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+        v[k] = i0 + k < n ? in[i0 + k] : 0;
+        s += v[k];
+    }
+    int total;
+    int run = sums[blockIdx.x] + block_exscan_int(s, total);
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+        if (i0 + k < n) out[i0 + k] = run;
+        run += v[k];
+    }
+}
+
+// ------------------------------------------------------------------------------ CSC assembly
+// Entry p of the sorted columns starts columns (previous column, column at p]: they all begin at p.
+// p = n_edges closes the remaining columns up to n_src.
+__global__ __launch_bounds__(kBlock) void csc_bounds_kernel(const int32_t* __restrict__ skeys, int64_t n_edges,
+                                                            int64_t n_src, int32_t* __restrict__ col_ptr) {
+    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p <= n_edges; p += (int64_t)gridDim.x * kBlock) {
+        const int64_t prev = p > 0 ? skeys[p - 1] : -1;
+        const int64_t cur = p < n_edges ? skeys[p] : n_src;
+        for (int64_t j = prev + 1; j <= cur; ++j) col_ptr[j] = (int32_t)p;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void gather_rows_kernel(const int32_t* __restrict__ perm,
+                                                             const int32_t* __restrict__ rows, int64_t n,
+                                                             int32_t* __restrict__ row_idx) {
+    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n; p += (int64_t)gridDim.x * kBlock)
+        row_idx[p] = rows[perm[p]];
+}
+
+// dst[p,:] = src[perm[p],:] for [E,H] per-edge values
+template <int H>
+__global__ __launch_bounds__(kBlock) void permute_edges_kernel(const int32_t* __restrict__ perm,
+                                                               const float* __restrict__ src, int64_t n,
+                                                               float* __restrict__ dst) {
+    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n; p += (int64_t)gridDim.x * kBlock) {
+        const int64_t e = perm[p];
+        if constexpr (H % 4 == 0) {
+#pragma unroll
+            for (int h = 0; h < H; h += 4)
+                *reinterpret_cast<float4*>(dst + p * H + h) = *reinterpret_cast<const float4*>(src + e * H + h);
+        } else {
+#pragma unroll
+            for (int h = 0; h < H; ++h) dst[p * H + h] = src[e * H + h];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ edge dots
+// Per edge e (row i = rows[e], source j = col[e]) and head h: out[e,h] = <G[i,h,:], F[j,h,:]>,
+// G fp32.  A slot of lanes holds one edge (the geometry of F's rows); each lane reads NV 16-byte
+// pieces of F and the matching EPP floats of G; the head sums stay in registers (group_sum).
+
+template <typename T, int H, int D>
+__global__ __launch_bounds__(kBlock) void edge_dot_kernel(const int32_t* __restrict__ rows,
+                                                          const int32_t* __restrict__ col, int64_t n_edges,
+                                                          const float* __restrict__ gf, const T* __restrict__ ff,
+                                                          float* __restrict__ out) {
+    using Gm = Geo<T, H, D>;
+    constexpr int G = Gm::G, P = Gm::P, NV = Gm::NV, EPP = Gm::EPP, LPH = Gm::LPH, HD = Gm::HD;
+    constexpr int UMAX = (4 / NV) > 1 ? (4 / NV) : 1;
+    constexpr int U = UMAX * P <= kWave ? UMAX : kWave / P;
+    constexpr int EPI = U * P;   // edges per wave iteration (<= 64: one index per lane)
+    const int lane = lane_id();
+    const int q = lane % G, g = lane / G;
+    int hv[NV], off[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        hv[v] = (v * G + q) / LPH;
+        off[v] = (v * G + q) * EPP;
+    }
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t base = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * EPI; base < n_edges;
+         base += nwaves * EPI) {
+        int ri = 0, ci = 0;
+        if (lane < EPI && base + lane < n_edges) {
+            ri = rows[base + lane];
+            ci = col[base + lane];
+        }
+        uint4 fa[U][NV];
+        float4 ga[U][NV][EPP / 4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int el = u * P + g;
+            const int r_i = shfl(ri, el), c_i = shfl(ci, el);
+            const bool valid = base + el < n_edges;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                if (valid) {
+                    fa[u][v] = ld16(ff + (int64_t)c_i * HD + off[v]);
+#pragma unroll
+                    for (int k = 0; k < EPP / 4; ++k)
+                        ga[u][v][k] = *reinterpret_cast<const float4*>(gf + (int64_t)r_i * HD + off[v] + 4 * k);
+                } else {
+                    fa[u][v] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                    for (int k = 0; k < EPP / 4; ++k) ga[u][v][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int el = u * P + g;
+            const int64_t e = base + el;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float f[EPP];
+                unpack<T>(fa[u][v], f);
+                float d = 0.f;
+#pragma unroll
+                for (int k = 0; k < EPP / 4; ++k) {
+                    d = fmaf(ga[u][v][k].x, f[4 * k], d);
+                    d = fmaf(ga[u][v][k].y, f[4 * k + 1], d);
+                    d = fmaf(ga[u][v][k].z, f[4 * k + 2], d);
+                    d = fmaf(ga[u][v][k].w, f[4 * k + 3], d);
+                }
+                d = group_sum<LPH>(d);
+                if (e < n_edges && (v * G + q) % LPH == 0) out[e * H + hv[v]] = d;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ softmax backward
+// out[e,h] = scale * alpha[e,h] * (g[e,h] - sum_{e' in row} alpha[e',h] * g[e',h]); out may alias g.
+constexpr int kSbG = 32;                  // lanes per row slot: lane q reads edge q/H, head q%H
+constexpr int kSbRowsPerWave = 32;
+
+// rows with deg <= hi (all rows when there is no plan), a 32-lane slot per row: one pass for the
+// per-head dot, one for the output
+template <int H>
+__global__ __launch_bounds__(kBlock) void softmax_bwd_short_kernel(const int32_t* __restrict__ row_ptr,
+                                                                   int64_t n_rows, const float* alpha,
+                                                                   const float* grad, float* out, int hi,
+                                                                   float scale) {
+    constexpr int SC = kSbG / H;
+    const int lane = lane_id();
+    const int64_t wb = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * kSbRowsPerWave;
+    if (wb >= n_rows) return;
+    int rpv = 0;
+    if (lane <= kSbRowsPerWave && wb + lane <= n_rows) rpv = row_ptr[wb + lane];
+    const int q = lane % kSbG, g = lane / kSbG, es = q / H;
+#pragma unroll 1
+    for (int it = 0; it < kSbRowsPerWave / (kWave / kSbG); ++it) {
+        const int j = it * (kWave / kSbG) + g;
+        int e0 = shfl(rpv, j), e1 = shfl(rpv, j + 1);
+        if (!(wb + j < n_rows && e1 - e0 <= hi)) e1 = e0;
+        float s = 0.f;
+        for (int c = e0; c < e1; c += SC)
+            if (c + es < e1) {
+                const int64_t i = (int64_t)c * H + q;
+                s = fmaf(alpha[i], grad[i], s);
+            }
+#pragma unroll
+        for (int o = H; o < kSbG; o <<= 1) s += shfl_xor(s, o);
+        for (int c = e0; c < e1; c += SC)
+            if (c + es < e1) {
+                const int64_t i = (int64_t)c * H + q;
+                out[i] = scale * alpha[i] * (grad[i] - s);
+            }
+    }
+}
+
+// workgroup-wide per-head sum of one float per thread, where thread t holds head t % H
+template <int H>
+__device__ __forceinline__ float block_head_sum(float s, float (*ls)[H]) {
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+#pragma unroll
+    for (int o = H; o < kWave; o <<= 1) s += shfl_xor(s, o);
+    if (lane < H) ls[w][lane] = s;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i) t += ls[i][threadIdx.x % H];
+    __syncthreads();
+    return t;
+}
+
+// one workgroup per plan segment: thread t takes elements t, t+256, ... (all of head t % H);
+// a long row is written here, a hub segment leaves its per-head dot in the partial buffer
+template <int H>
+__global__ __launch_bounds__(kBlock) void softmax_bwd_segment_kernel(const float* alpha, const float* grad,
+                                                                     float* out, PlanView plan, float scale) {
+    __shared__ float ls[kWavesPerBlock][H];
+    const int t = threadIdx.x;
+    const int n_segs = plan.counts[kNSegs];
+    for (int s = blockIdx.x; s < n_segs; s += gridDim.x) {
+        const int4 sg = plan.segs[s];
+        const int64_t b = (int64_t)sg.y * H, e = (int64_t)sg.z * H;
+        float acc = 0.f;
+        for (int64_t i = b + t; i < e; i += kBlock) acc = fmaf(alpha[i], grad[i], acc);
+        const float dot = block_head_sum<H>(acc, ls);
+        if (sg.w < 0) {
+            for (int64_t i = b + t; i < e; i += kBlock) out[i] = scale * alpha[i] * (grad[i] - dot);
+        } else if (t < H) {
+            plan.partials[(int64_t)sg.w * plan.state_floats + t] = dot;
+        }
+    }
+}
+
+// one workgroup per hub segment: the hub's dot is the sum of its segments' partials
+template <int H>
+__global__ __launch_bounds__(kBlock) void softmax_bwd_hub_kernel(const int32_t* __restrict__ row_ptr,
+                                                                 const float* alpha, const float* grad, float* out,
+                                                                 PlanView plan, float scale) {
+    __shared__ float ls[kWavesPerBlock][H];
+    const int t = threadIdx.x;
+    const int n_hub_segs = plan.counts[kNHubSegs];
+    for (int s = blockIdx.x; s < n_hub_segs; s += gridDim.x) {
+        const int4 sg = plan.segs[s];   // row, b, e, slot (= s)
+        const int rb = row_ptr[sg.x], re = row_ptr[sg.x + 1];
+        const int first = sg.w - (int)(((int64_t)sg.y - rb) / plan.seg_len);
+        const int nseg = (int)(((int64_t)re - rb + plan.seg_len - 1) / plan.seg_len);
+        // kBlock is a multiple of H: thread t sums head t % H over segments t / H, t / H + 256 / H, ...
+        float acc = 0.f;
+        for (int c = t / H; c < nseg; c += kBlock / H)
+            acc += plan.partials[(int64_t)(first + c) * plan.state_floats + t % H];
+        const float dot = block_head_sum<H>(acc, ls);
+        for (int64_t i = (int64_t)sg.y * H + t; i < (int64_t)sg.z * H; i += kBlock)
+            out[i] = scale * alpha[i] * (grad[i] - dot);
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ launchers
+hipError_t launch_expand_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    const int64_t waves = (n_rows + kWave - 1) / kWave;
+    hipLaunchKernelGGL(expand_rows_kernel, dim3(grid_for(waves, kWavesPerBlock, INT32_MAX)), dim3(kBlock), 0, stream,
+                       row_ptr, n_rows, rows);
+    return hipGetLastError();
+}
+
+int64_t radix_tiles(int64_t n) { return (n + kSortTile - 1) / kSortTile; }
+int64_t scan_tiles(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
+
+hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* sums, int32_t* out, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int64_t nb = scan_tiles(n);
+    hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(kBlock), 0, stream, in, n, sums);
+    hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(kBlock), 0, stream, sums, nb);
+    hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)nb), dim3(kBlock), 0, stream, in, n, sums, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout, int64_t n,
+                             int shift, int32_t* hist, int32_t* sums, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int64_t nt = radix_tiles(n);
+    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, n, shift, hist, nt);
+    const hipError_t e = launch_exclusive_scan(hist, nt * kRadixBins, sums, hist, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, vin, kout, vout, n,
+                       shift, hist, nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
+                             int64_t n_src, int32_t* col_ptr, int32_t* row_idx, hipStream_t stream) {
+    hipLaunchKernelGGL(csc_bounds_kernel, dim3(grid_for(n_edges + 1, kBlock, 65536)), dim3(kBlock), 0, stream, skeys,
+                       n_edges, n_src, col_ptr);
+    if (n_edges > 0)
+        hipLaunchKernelGGL(gather_rows_kernel, dim3(grid_for(n_edges, kBlock, 65536)), dim3(kBlock), 0, stream, perm,
+                           rows, n_edges, row_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float* dst,
+                                hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const bool ok = dispatch_heads(H, [&](auto tag) {
+        constexpr int HH = decltype(tag)::H;
+        hipLaunchKernelGGL(permute_edges_kernel<HH>, dim3(grid_for(n, kBlock, 65536)), dim3(kBlock), 0, stream, perm,
+                           src, n, dst);
+    });
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_edge_dot(int dtype, int H, int D, const int32_t* rows, const int32_t* col, int64_t n_edges,
+                           const float* gf, const void* ff, float* out, hipStream_t stream) {
+    if (n_edges == 0) return hipSuccess;
+    const bool ok = dispatch_shape(dtype, H, D, [&](auto tag) {
+        using Tag = decltype(tag);
+        using T = typename Tag::type;
+        using Gm = Geo<T, Tag::H, Tag::D>;
+        constexpr int UMAX = (4 / Gm::NV) > 1 ? (4 / Gm::NV) : 1;
+        constexpr int U = UMAX * Gm::P <= kWave ? UMAX : kWave / Gm::P;
+        const int64_t waves = (n_edges + U * Gm::P - 1) / (U * Gm::P);
+        hipLaunchKernelGGL((edge_dot_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, 65536)),
+                           dim3(kBlock), 0, stream, rows, col, n_edges, gf, static_cast<const T*>(ff), out);
+    });
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows, const float* alpha,
+                                   const float* grad, float* out, float scale, const PlanView* plan,
+                                   hipStream_t stream) {
+    const bool ok = dispatch_heads(H, [&](auto tag) {
+        constexpr int HH = decltype(tag)::H;
+        if (plan)
+            hipLaunchKernelGGL(softmax_bwd_segment_kernel<HH>,
+                               dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
+                               alpha, grad, out, *plan, scale);
+        const int64_t waves = (n_rows + kSbRowsPerWave - 1) / kSbRowsPerWave;
+        hipLaunchKernelGGL(softmax_bwd_short_kernel<HH>, dim3(grid_for(waves, kWavesPerBlock, INT32_MAX)),
+                           dim3(kBlock), 0, stream, row_ptr, n_rows, alpha, grad, out,
+                           plan ? plan->short_max : INT32_MAX, scale);
+        if (plan)
+            hipLaunchKernelGGL(softmax_bwd_hub_kernel<HH>,
+                               dim3(grid_for(plan->hubseg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
+                               row_ptr, alpha, grad, out, *plan, scale);
+    });
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gat

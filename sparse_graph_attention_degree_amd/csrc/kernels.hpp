@@ -97,6 +97,36 @@ hipError_t launch_spmm(int mode, int dtype, int H, int D, const int32_t* row_ptr
                        int64_t n_rows, int64_t n_src, const float* scores, const void* q, const void* k, const void* v,
                        float scale, float* out, const PlanView* plan, hipStream_t stream);
 
+// ---------------------------------------------------------------------------- backward
+hipError_t launch_expand_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* rows, hipStream_t stream);
+
+// radix sort of (column, edge id): tiles per pass, and tiles of the scan of the digit counts
+int64_t radix_tiles(int64_t n);
+int64_t scan_tiles(int64_t n);
+constexpr int kRadixDigitBits = 4;
+constexpr int kRadixDigits = 1 << kRadixDigitBits;
+
+// one stable pass on bits [shift, shift+4) of the keys; vin == nullptr means values = positions.
+// hist: int32 [16 * radix_tiles(n)], sums: int32 [scan_tiles(16 * radix_tiles(n))].
+hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout, int64_t n,
+                             int shift, int32_t* hist, int32_t* sums, hipStream_t stream);
+
+// col_ptr [n_src+1] from the sorted columns; row_idx[p] = rows[perm[p]]
+hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
+                             int64_t n_src, int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
+
+hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float* dst,
+                                hipStream_t stream);
+
+// out[e,h] = <G[rows[e],h,:], F[col[e],h,:]>, G fp32 [*,H,D], F of dtype
+hipError_t launch_edge_dot(int dtype, int H, int D, const int32_t* rows, const int32_t* col, int64_t n_edges,
+                           const float* gf, const void* ff, float* out, hipStream_t stream);
+
+// out = scale * alpha * (grad - sum_row alpha * grad)
+hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows, const float* alpha,
+                                   const float* grad, float* out, float scale, const PlanView* plan,
+                                   hipStream_t stream);
+
 // Rows per binner block (256 threads x 4 consecutive rows).
 constexpr int kPlanRowsPerThread = 4;
 constexpr int kPlanRowsPerBlock = kBlock * kPlanRowsPerThread;

@@ -23,7 +23,9 @@ DEFAULT_SHORT_MAX = 64
 DEFAULT_SEG_LEN = 1024
 
 EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge_softmax", "gat_aggregate",
-            "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof"]
+            "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof",
+            "gat_csc_workspace_bytes", "gat_csc_sizeof", "gat_csc_build", "gat_edge_softmax_backward",
+            "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward"]
 
 
 class GatError(RuntimeError):
@@ -46,6 +48,16 @@ class GatPlanStruct(ctypes.Structure):
                 ("magic", ctypes.c_uint32)]
 
 
+class GatCscStruct(ctypes.Structure):
+    """Mirror of ``gat_csc`` (checked against gat_csc_sizeof at load)."""
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_src", ctypes.c_int64), ("n_edges", ctypes.c_int64),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("off_col_ptr", ctypes.c_size_t), ("off_row_idx", ctypes.c_size_t), ("off_perm", ctypes.c_size_t),
+                ("off_rows", ctypes.c_size_t), ("off_stage", ctypes.c_size_t),
+                ("plan", GatPlanStruct), ("magic", ctypes.c_uint32)]
+
+
 _LIB = None
 
 
@@ -64,7 +76,18 @@ def _lib():
     L.gat_edge_softmax.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     L.gat_aggregate.argtypes = [vp, vp, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp]
     L.gat_fused_layer.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, vp]
-    for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer):
+    L.gat_csc_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.gat_csc_workspace_bytes.restype = sz
+    L.gat_csc_sizeof.restype = sz
+    L.gat_csc_build.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, ctypes.POINTER(GatCscStruct), vp]
+    L.gat_edge_softmax_backward.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
+    L.gat_aggregate_backward.argtypes = [vp, vp, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.gat_layer_backward_workspace_bytes.argtypes = [i64, i32]
+    L.gat_layer_backward_workspace_bytes.restype = sz
+    L.gat_fused_layer_backward.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer,
+              L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward):
         f.restype = i32
     L.gat_status_str.argtypes = [i32]
     L.gat_status_str.restype = ctypes.c_char_p
@@ -73,6 +96,8 @@ def _lib():
     L.gat_plan_sizeof.restype = sz
     if L.gat_plan_sizeof() != ctypes.sizeof(GatPlanStruct):
         raise RuntimeError("gat_plan layout mismatch between libgat.so and the binding")
+    if L.gat_csc_sizeof() != ctypes.sizeof(GatCscStruct):
+        raise RuntimeError("gat_csc layout mismatch between libgat.so and the binding")
     _LIB = L
     return L
 
@@ -235,3 +260,124 @@ def gat_fused_layer(row_ptr, col_idx, v, scores=None, q=None, k=None, scale: flo
                                                      _ptr(k), float(scale), _ptr(v), _ptr(out),
                                                      plan.ref() if plan else None, _stream(stream)))
     return out
+
+
+# ----------------------------------------------------------------------------- backward
+class Csc:
+    """The transposed view of a graph (gat_csc) plus the device workspace that holds it."""
+
+    def __init__(self, struct: GatCscStruct, ws: torch.Tensor):
+        self.struct = struct
+        self.ws = ws
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+    def table(self, which: str) -> torch.Tensor:
+        """View of a CSC array in the workspace (int32), for inspection."""
+        s = self.struct
+        n = {"col_ptr": s.n_src + 1, "row_idx": s.n_edges, "perm": s.n_edges, "rows": s.n_edges}[which]
+        off = {"col_ptr": s.off_col_ptr, "row_idx": s.off_row_idx, "perm": s.off_perm, "rows": s.off_rows}[which]
+        return self.ws[off:off + 4 * n].view(torch.int32)
+
+
+def gat_csc_workspace_bytes(n_rows, n_src, n_edges, heads, head_dim) -> int:
+    return int(_lib().gat_csc_workspace_bytes(n_rows, n_src, n_edges, heads, head_dim))
+
+
+def gat_csc_build(row_ptr, col_idx, n_src: int, heads: int, head_dim: int, ws: torch.Tensor | None = None,
+                  stream=None) -> Csc:
+    """Build the transposed view on the device (no synchronisation); allocates the workspace with
+    torch unless ``ws`` (uint8, 256-byte aligned) is given."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(col_idx, "col_idx", torch.int32, 1)
+    n_rows, E = row_ptr.numel() - 1, col_idx.numel()
+    need = gat_csc_workspace_bytes(n_rows, n_src, E, heads, head_dim)
+    if need == 0:
+        raise GatError("gat_csc_workspace_bytes", 2)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=row_ptr.device)
+    _dev(ws, "ws", torch.uint8, 1)
+    st = GatCscStruct()
+    _check("gat_csc_build", _lib().gat_csc_build(_ptr(row_ptr), _ptr(col_idx), n_rows, n_src, E, heads, head_dim,
+                                                 _ptr(ws), ws.numel(), ctypes.byref(st), _stream(stream)))
+    return Csc(st, ws)
+
+
+def gat_edge_softmax_backward(row_ptr, alpha, grad, out=None, plan: Plan | None = None, stream=None):
+    """dL/dscores = alpha * (grad - sum_row alpha * grad), fp32 [E,H]; ``out`` may be ``grad``."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(alpha, "alpha", torch.float32, 2)
+    _dev(grad, "grad", torch.float32, 2)
+    E, H = alpha.shape
+    if grad.shape != alpha.shape:
+        raise ValueError("alpha and grad differ in shape")
+    if out is None:
+        out = torch.empty_like(alpha)
+    _dev(out, "out", torch.float32, 2)
+    _check("gat_edge_softmax_backward",
+           _lib().gat_edge_softmax_backward(_ptr(row_ptr), row_ptr.numel() - 1, E, H, _ptr(alpha), _ptr(grad),
+                                            _ptr(out), plan.ref() if plan else None, _stream(stream)))
+    return out
+
+
+def gat_aggregate_backward(row_ptr, col_idx, weights, feat, grad_out, csc: Csc, dweights=True, dfeat=True,
+                           stream=None):
+    """(dL/dweights fp32 [E,H] or None, dL/dfeat fp32 [n_src,H,D] or None).  ``dweights`` / ``dfeat``:
+    True (allocate), False (skip) or an output tensor."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(col_idx, "col_idx", torch.int32, 1)
+    _dev(weights, "weights", torch.float32, 2)
+    _dev(feat, "feat", None, 3)
+    _dev(grad_out, "grad_out", torch.float32, 3)
+    n_rows, E = row_ptr.numel() - 1, col_idx.numel()
+    ns, H, D = feat.shape
+    if dweights is True:
+        dweights = torch.empty((E, H), dtype=torch.float32, device=feat.device)
+    if dfeat is True:
+        dfeat = torch.empty((ns, H, D), dtype=torch.float32, device=feat.device)
+    dweights = dweights if isinstance(dweights, torch.Tensor) else None
+    dfeat = dfeat if isinstance(dfeat, torch.Tensor) else None
+    _dev(dweights, "dweights", torch.float32, 2)
+    _dev(dfeat, "dfeat", torch.float32, 3)
+    _check("gat_aggregate_backward",
+           _lib().gat_aggregate_backward(_ptr(row_ptr), _ptr(col_idx), n_rows, ns, E, _ptr(weights), _ptr(feat),
+                                         _feat_dtype(feat), H, D, _ptr(grad_out), _ptr(dweights), _ptr(dfeat),
+                                         csc.ref(), _stream(stream)))
+    return dweights, dfeat
+
+
+def gat_layer_backward_workspace_bytes(n_edges, heads) -> int:
+    return int(_lib().gat_layer_backward_workspace_bytes(n_edges, heads))
+
+
+def gat_fused_layer_backward(row_ptr, col_idx, v, grad_out, plan: Plan, csc: Csc, scores=None, q=None, k=None,
+                             scale: float = 1.0, ws: torch.Tensor | None = None, stream=None):
+    """Gradients of gat_fused_layer: (dscores, None, None, dv) with scores, or (None, dq, dk, dv) with q, k."""
+    for t, name in ((row_ptr, "row_ptr"), (col_idx, "col_idx")):
+        _dev(t, name, torch.int32, 1)
+    _dev(v, "v", None, 3)
+    _dev(grad_out, "grad_out", torch.float32, 3)
+    _dev(scores, "scores", torch.float32, 2)
+    _dev(q, "q", v.dtype, 3)
+    _dev(k, "k", v.dtype, 3)
+    n_rows, E = row_ptr.numel() - 1, col_idx.numel()
+    ns, H, D = v.shape
+    dev = v.device
+    need = gat_layer_backward_workspace_bytes(E, H)
+    if need == 0:
+        raise GatError("gat_layer_backward_workspace_bytes", 2)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(ws, "ws", torch.uint8, 1)
+    layer = scores is None
+    dscores = None if layer else torch.empty((E, H), dtype=torch.float32, device=dev)
+    dq = torch.empty((n_rows, H, D), dtype=torch.float32, device=dev) if layer else None
+    dk = torch.empty((ns, H, D), dtype=torch.float32, device=dev) if layer else None
+    dv = torch.empty((ns, H, D), dtype=torch.float32, device=dev)
+    _check("gat_fused_layer_backward",
+           _lib().gat_fused_layer_backward(_ptr(row_ptr), _ptr(col_idx), n_rows, ns, E, H, D, _feat_dtype(v),
+                                           _ptr(scores), _ptr(q), _ptr(k), float(scale), _ptr(v),
+                                           _ptr(grad_out), _ptr(dscores), _ptr(dq), _ptr(dk), _ptr(dv), plan.ref(),
+                                           csc.ref(), _ptr(ws), ws.numel(), _stream(stream)))
+    return dscores, dq, dk, dv

@@ -157,3 +157,59 @@ def test_binning_reference_tiles_rows():
         assert covered.sum() == sum(deg[i] for i in nonshort)
         assert nhs == sum(-(-deg[i] // seg_len) for i in np.flatnonzero(cls == 2))
         assert np.all(segs[:nhs, 3] == np.arange(nhs)) and np.all(segs[nhs:, 3] == -1)
+
+
+def test_csc_struct_layout_and_workspace(L):
+    assert L.gat_csc_sizeof() == ctypes.sizeof(gat.GatCscStruct)
+    assert L.gat_csc_workspace_bytes(-1, 4, 4, 4, 64) == 0
+    assert L.gat_csc_workspace_bytes(4, 4, 2**31, 4, 64) == 0
+    assert L.gat_csc_workspace_bytes(4, 4, 4, 3, 64) == 0
+    a = L.gat_csc_workspace_bytes(2**20, 2**20, 2**24, 4, 64)
+    assert a > 6 * 4 * 2**24 and a % 256 == 0
+    assert L.gat_csc_workspace_bytes(0, 0, 0, 1, 16) > 0
+    assert L.gat_layer_backward_workspace_bytes(-1, 4) == 0
+    assert L.gat_layer_backward_workspace_bytes(4, 3) == 0
+    assert L.gat_layer_backward_workspace_bytes(2**24, 4) >= 3 * 4 * 4 * 2**24
+    assert L.gat_layer_backward_workspace_bytes(0, 4) > 0
+
+
+def test_csc_build_host_checks(L):
+    f = L.gat_csc_build
+    c = gat.GatCscStruct()
+    need = L.gat_csc_workspace_bytes(100, 80, 1000, 4, 64)
+    assert f(FAKE, FAKE, 100, 80, 1000, 4, 64, FAKE, need, None, None) == NULL
+    assert f(None, FAKE, 100, 80, 1000, 4, 64, FAKE, need, ctypes.byref(c), None) == NULL
+    assert f(FAKE, None, 100, 80, 1000, 4, 64, FAKE, need, ctypes.byref(c), None) == NULL
+    assert f(FAKE, FAKE, 100, 0, 1000, 4, 64, FAKE, need, ctypes.byref(c), None) == ARGS
+    assert f(FAKE, FAKE, 100, 80, 1000, 4, 64, ctypes.c_void_p(0x1010), need, ctypes.byref(c), None) == ARGS
+    assert f(FAKE, FAKE, 100, 80, 1000, 4, 64, FAKE, need - 1, ctypes.byref(c), None) == WS
+    assert f(FAKE, FAKE, 100, 80, 1000, 3, 64, FAKE, need, ctypes.byref(c), None) == UNSUP
+    assert f(FAKE, FAKE, 100, -80, 1000, 4, 64, FAKE, need, ctypes.byref(c), None) == SIZE
+
+
+def test_backward_host_checks(L):
+    bad_plan, bad_csc = gat.GatPlanStruct(), gat.GatCscStruct()   # magic not set
+    f = L.gat_edge_softmax_backward
+    assert f(FAKE, -1, 5, 1, FAKE, FAKE, FAKE, None, None) == SIZE
+    assert f(FAKE, 4, 5, 3, FAKE, FAKE, FAKE, None, None) == UNSUP
+    assert f(FAKE, 4, 5, 1, None, FAKE, FAKE, None, None) == NULL
+    assert f(FAKE, 4, 5, 1, FAKE, FAKE, None, None, None) == NULL
+    assert f(FAKE, 4, 5, 1, FAKE, FAKE, FAKE, ctypes.byref(bad_plan), None) == ARGS
+    assert f(None, 0, 0, 1, None, None, None, None, None) == OK
+    g = L.gat_aggregate_backward
+    assert g(FAKE, FAKE, 4, 4, 5, FAKE, FAKE, 0, 1, 64, FAKE, FAKE, FAKE, None, None) == NULL        # no csc
+    assert g(FAKE, FAKE, 4, 4, 5, FAKE, FAKE, 0, 1, 64, FAKE, FAKE, FAKE, ctypes.byref(bad_csc), None) == ARGS
+    assert g(FAKE, FAKE, 4, 4, 5, FAKE, FAKE, 0, 1, 48, FAKE, FAKE, FAKE, ctypes.byref(bad_csc), None) == UNSUP
+    assert g(FAKE, FAKE, 4, 4, -5, FAKE, FAKE, 0, 1, 64, FAKE, FAKE, FAKE, ctypes.byref(bad_csc), None) == SIZE
+    h = L.gat_fused_layer_backward
+
+    def hargs(sc, q, k, plan, csc, heads=4):
+        return (FAKE, FAKE, 4, 4, 5, heads, 64, 0, sc, q, k, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                plan, csc, FAKE, 1 << 20, None)
+    pr, cr = ctypes.byref(bad_plan), ctypes.byref(bad_csc)
+    assert h(*hargs(FAKE, FAKE, FAKE, pr, cr)) == ARGS          # both modes
+    assert h(*hargs(None, None, None, pr, cr)) == ARGS          # neither
+    assert h(*hargs(FAKE, None, None, None, cr)) == NULL        # plan required
+    assert h(*hargs(FAKE, None, None, pr, None)) == NULL        # csc required
+    assert h(*hargs(FAKE, None, None, pr, cr)) == ARGS          # plan not built
+    assert h(*hargs(FAKE, None, None, pr, cr, heads=3)) == UNSUP
