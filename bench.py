@@ -158,6 +158,44 @@ def copy_rate(nbytes=1 << 30, reps=5):
     return 2 * nbytes / t / 1e9
 
 
+def bench_backward(gat, rp, col, qd, kd, vd, scores, N, E, H, D, feat_bytes, stream, reps=5):
+    """The backward rows over the same graph, each timed alone with HIP events (mean of reps):
+    the transposed-graph build, and the full-layer backward (dq, dk, dv)."""
+    import torch
+    out = {}
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    csc_ws = torch.empty(gat.gat_csc_workspace_bytes(N, N, E, H, D), dtype=torch.uint8, device=vd.device)
+    csc = gat.gat_csc_build(rp, col, N, H, D, ws=csc_ws)
+    t = timed(lambda: gat.gat_csc_build(rp, col, N, H, D, ws=csc_ws))
+    out["csc_build_ms"] = t * 1e3
+    plan = gat.gat_plan_build(rp, E, H, D)
+    go = torch.randn((N, H, D), dtype=torch.float32, device=vd.device)
+    ws = torch.empty(gat.gat_layer_backward_workspace_bytes(E, H), dtype=torch.uint8, device=vd.device)
+    t = timed(lambda: gat.gat_fused_layer_backward(rp, col, vd, go, plan, csc, q=qd, k=kd, ws=ws))
+    # compulsory bytes: rows gathered per edge -- k (score recompute), v (dL/dalpha), k (dq), q (dk) and
+    # grad_out (dv) --, q and grad_out read once per row, dq/dk/dv written, 14 passes over [E,H] fp32
+    # arrays (scores, alpha, dL/dalpha, g_s and their CSC copies) and 9 over int32 [E] index arrays
+    fb, hd = feat_bytes, H * D
+    alg = (4 * E * hd * fb + E * hd * 4 + N * hd * fb + N * hd * 4 + 3 * N * hd * 4 + 14 * 4 * E * H
+           + 9 * 4 * E)
+    out["layer_backward_ms"] = t * 1e3
+    out["layer_backward_edge_heads_per_s"] = E * H / t
+    out["layer_backward_alg_bytes"] = alg
+    out["layer_backward_gbs"] = alg / t / 1e9
+    return out
+
+
 def bench_coo(args, w, gat, G):
     """COO workload: one step = one SDDMM over the edge list."""
     import torch
@@ -224,6 +262,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--backward", action="store_true", help="also time the transposed-graph build and the "
+                                                              "full-layer backward")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -370,6 +410,9 @@ def main():
             extra[f"{name}_edge_heads_per_s"] = E * H / t
             extra[f"{name}_alg_bytes"] = nbytes
             extra[f"{name}_gbs"] = nbytes / t / 1e9
+
+    if args.backward:
+        extra.update(bench_backward(gat, rp, col, qd, kd, vd, scores, N, E, H, D, feat_bytes, stream))
 
     cpu = None
     if not args.no_cpu:
