@@ -180,6 +180,24 @@ int gat_shape_supported(int heads, int head_dim);
 /* sizeof(gat_plan) as compiled into the library, for bindings that mirror the struct (host). */
 size_t gat_plan_sizeof(void);
 
+/*
+ * Batch of B CSR graphs as one block-diagonal CSR, assembled on the device.  The l2_p37 page
+ * judges its 384-node problem too small for the launch overhead; batched, any number of such graphs
+ * is one graph, every entry point above covers the batch in the launches of one call, and each
+ * row's result is the same as in its own graph (bit for bit: a row only meets its own edges).
+ * Inputs (device, int32): the B graphs' own arrays concatenated -- local_row_ptr [sum_b (N_b+1)]
+ * (graph b's row_ptr, starting at 0) and local_col [sum_b E_b] (its source ids, < Ns_b) -- and the
+ * prefix sums row_off, edge_off, src_off [B+1] of N_b, E_b, Ns_b (row_off[B] = n_rows,
+ * edge_off[B] = n_edges).  Outputs (device, int32): row_ptr [n_rows+1] with
+ * row_ptr[row_off[b] + i] = edge_off[b] + (graph b's row_ptr[i]), and col_idx [n_edges] with
+ * col_idx[edge_off[b] + e] = src_off[b] + (graph b's col[e]).  Features of the batch are the
+ * graphs' tables stacked in the same order.  Enqueued on `stream`; the offsets are not checked on
+ * the device.
+ */
+gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col, const int32_t* row_off,
+                         const int32_t* edge_off, const int32_t* src_off, int64_t n_graphs, int64_t n_rows,
+                         int64_t n_edges, int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Backward.  No page writes the backward pass out; the l1_p10 page (edge-only SDDMM, the
  * passage on the backward pass) notes that gradients sum into the feature rows that edges read.

@@ -343,6 +343,16 @@ gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64
                                        scale, out, plan ? &pv : nullptr, stream));
 }
 
+gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col, const int32_t* row_off,
+                         const int32_t* edge_off, const int32_t* src_off, int64_t n_graphs, int64_t n_rows,
+                         int64_t n_edges, int32_t* row_ptr, int32_t* col_idx, hipStream_t stream) {
+    if (n_graphs < 1 || n_graphs > kMaxIndex || !size_ok(n_rows) || !edges_ok(n_edges)) return GAT_ERR_SIZE;
+    if (!local_row_ptr || !row_off || !edge_off || !row_ptr) return GAT_ERR_NULL;
+    if (n_edges > 0 && (!local_col || !src_off || !col_idx)) return GAT_ERR_NULL;
+    return hip_status(gat::launch_batch_csr(local_row_ptr, local_col, row_off, edge_off, src_off, n_graphs, n_rows,
+                                            n_edges, row_ptr, col_idx, stream));
+}
+
 // ------------------------------------------------------------------------------ backward
 size_t gat_csc_sizeof(void) { return sizeof(gat_csc); }
 

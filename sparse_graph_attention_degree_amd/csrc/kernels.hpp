@@ -127,6 +127,11 @@ hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows
                                    const float* grad, float* out, float scale, const PlanView* plan,
                                    hipStream_t stream);
 
+// block-diagonal batch of CSR graphs (offsets: device int32 [n_graphs+1] prefix sums)
+hipError_t launch_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col, const int32_t* row_off,
+                            const int32_t* edge_off, const int32_t* src_off, int64_t n_graphs, int64_t n_rows,
+                            int64_t n_edges, int32_t* row_ptr, int32_t* col, hipStream_t stream);
+
 // Rows per binner block (256 threads x 4 consecutive rows).
 constexpr int kPlanRowsPerThread = 4;
 constexpr int kPlanRowsPerBlock = kBlock * kPlanRowsPerThread;

@@ -25,7 +25,8 @@ DEFAULT_SEG_LEN = 1024
 EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge_softmax", "gat_aggregate",
             "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof",
             "gat_csc_workspace_bytes", "gat_csc_sizeof", "gat_csc_build", "gat_edge_softmax_backward",
-            "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward"]
+            "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward",
+            "gat_batch_csr"]
 
 
 class GatError(RuntimeError):
@@ -86,8 +87,10 @@ def _lib():
     L.gat_layer_backward_workspace_bytes.restype = sz
     L.gat_fused_layer_backward.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp,
                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gat_batch_csr.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer,
-              L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward):
+              L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward,
+              L.gat_batch_csr):
         f.restype = i32
     L.gat_status_str.argtypes = [i32]
     L.gat_status_str.restype = ctypes.c_char_p
@@ -381,3 +384,23 @@ def gat_fused_layer_backward(row_ptr, col_idx, v, grad_out, plan: Plan, csc: Csc
                                            _ptr(grad_out), _ptr(dscores), _ptr(dq), _ptr(dk), _ptr(dv), plan.ref(),
                                            csc.ref(), _ptr(ws), ws.numel(), _stream(stream)))
     return dscores, dq, dk, dv
+
+
+# ----------------------------------------------------------------------------- batching
+def gat_batch_csr(local_row_ptr, local_col, row_off, edge_off, src_off, stream=None):
+    """Block-diagonal CSR of B graphs from their concatenated arrays and int32 offsets [B+1]
+    (prefix sums of rows, edges and sources); returns (row_ptr, col_idx)."""
+    for t, name in ((local_row_ptr, "local_row_ptr"), (local_col, "local_col"), (row_off, "row_off"),
+                    (edge_off, "edge_off"), (src_off, "src_off")):
+        _dev(t, name, torch.int32, 1)
+    B = row_off.numel() - 1
+    if edge_off.numel() != B + 1 or src_off.numel() != B + 1:
+        raise ValueError("offset arrays differ in length")
+    n_rows = local_row_ptr.numel() - B
+    n_edges = local_col.numel()
+    row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=row_off.device)
+    col = torch.empty(n_edges, dtype=torch.int32, device=row_off.device)
+    _check("gat_batch_csr", _lib().gat_batch_csr(_ptr(local_row_ptr), _ptr(local_col), _ptr(row_off),
+                                                 _ptr(edge_off), _ptr(src_off), B, n_rows, n_edges, _ptr(row_ptr),
+                                                 _ptr(col), _stream(stream)))
+    return row_ptr, col

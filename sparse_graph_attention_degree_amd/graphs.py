@@ -336,6 +336,29 @@ def take_rows(g: CsrGraph, rows: np.ndarray):
     return sub_rp.astype(np.int32), g.col_idx[edge_ids], edge_ids
 
 
+def batch_arrays(graphs):
+    """The inputs of a block-diagonal batch: the graphs' row_ptr and col_idx concatenated as they
+    are, and int32 prefix sums [B+1] of their rows, edges and sources."""
+    local_rp = np.concatenate([g.row_ptr for g in graphs]).astype(np.int32)
+    local_col = np.concatenate([g.col_idx for g in graphs] + [np.zeros(0, np.int32)]).astype(np.int32)
+    off = lambda xs: np.concatenate([[0], np.cumsum(xs)]).astype(np.int32)  # noqa: E731
+    return (local_rp, local_col, off([g.n_rows for g in graphs]), off([g.n_edges for g in graphs]),
+            off([g.n_src for g in graphs]))
+
+
+def block_diagonal(graphs) -> CsrGraph:
+    """The batch as one CSR: graph b's rows, edges and sources shifted by the totals before it."""
+    rp = [np.zeros(1, np.int64)]
+    cols = [np.zeros(0, np.int32)]
+    e0 = s0 = 0
+    for g in graphs:
+        rp.append(g.row_ptr[1:].astype(np.int64) + e0)
+        cols.append((g.col_idx.astype(np.int64) + s0).astype(np.int32))
+        e0 += g.n_edges
+        s0 += g.n_src
+    return CsrGraph(np.concatenate(rp).astype(np.int32), np.concatenate(cols), s0)
+
+
 def row_of_edge(row_ptr: np.ndarray) -> np.ndarray:
     """Destination row id of every edge (COO expansion of a CSR row pointer)."""
     deg = np.diff(row_ptr.astype(np.int64))

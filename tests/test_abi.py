@@ -213,3 +213,27 @@ def test_backward_host_checks(L):
     assert h(*hargs(FAKE, None, None, pr, None)) == NULL        # csc required
     assert h(*hargs(FAKE, None, None, pr, cr)) == ARGS          # plan not built
     assert h(*hargs(FAKE, None, None, pr, cr, heads=3)) == UNSUP
+
+
+def test_batch_csr_host_checks(L):
+    f = L.gat_batch_csr
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 5, FAKE, FAKE, None) == SIZE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, -4, 5, FAKE, FAKE, None) == SIZE
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 2, 4, 5, FAKE, FAKE, None) == NULL
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 2, 4, 5, FAKE, FAKE, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 5, None, FAKE, None) == NULL
+
+
+def test_block_diagonal_reference():
+    """The numpy batch statement: each graph's rows keep their degrees and shifted sources."""
+    r = np.random.default_rng(3)
+    gs = [G.random_csr(n, ns, 5, r) for n, ns in [(4, 3), (0, 2), (6, 1), (3, 0 + 5)]]
+    gs.append(G.csr_from_degrees(np.zeros(3, int), 4, r))
+    bd = G.block_diagonal(gs)
+    assert bd.n_rows == sum(g.n_rows for g in gs) and bd.n_src == sum(g.n_src for g in gs)
+    assert np.array_equal(bd.degrees(), np.concatenate([g.degrees() for g in gs]))
+    lrp, lcol, ro, eo, so = G.batch_arrays(gs)
+    for b, g in enumerate(gs):
+        assert np.array_equal(bd.col_idx[eo[b]:eo[b + 1]] - so[b], g.col_idx)
+        assert np.array_equal(bd.row_ptr[ro[b]:ro[b + 1] + 1] - eo[b], g.row_ptr)
+        assert np.array_equal(lrp[ro[b] + b:ro[b + 1] + b + 1], g.row_ptr)
