@@ -23,7 +23,8 @@ streaming device copy measured on the same GPU.
 The COO workload c2 (1024 x 128 / 768 x 128 fp32 tables, 16384 edges) has no CSR: its step is
 the SDDMM alone and its roofline is the SDDMM's.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c5|c3|c2|c1]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c5|c3|c2|c1] [--batch B]
+                       [--backward]
        python bench.py --mode copy      # plain-copy calibration target for the counters
 """
 from __future__ import annotations
@@ -262,6 +263,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=1, help="graphs of the workload (seeds seed..seed+B-1) "
+                                                          "batched as one block-diagonal graph")
     ap.add_argument("--backward", action="store_true", help="also time the transposed-graph build and the "
                                                               "full-layer backward")
     args = ap.parse_args()
@@ -289,13 +292,15 @@ def main():
         bench_coo(args, w, gat, G)
         return
     t0 = time.perf_counter()
-    g = G.make_graph(w, args.seed)
+    B = max(1, args.batch)
+    graphs = [G.make_graph(w, args.seed + b) for b in range(B)]
+    q = np.concatenate([G.make_features(w, gb.n_rows, args.seed + b, "q") for b, gb in enumerate(graphs)])
+    k = np.concatenate([G.make_features(w, gb.n_src, args.seed + b, "k") for b, gb in enumerate(graphs)])
+    v = np.concatenate([G.make_features(w, gb.n_src, args.seed + b, "v") for b, gb in enumerate(graphs)])
+    g = graphs[0] if B == 1 else G.block_diagonal(graphs)
     N, E, H, D = g.n_rows, g.n_edges, w.heads, w.head_dim
     feat_bytes = 2 if w.dtype == "bf16" else 4
-    q = G.make_features(w, N, args.seed, "q")
-    k = G.make_features(w, g.n_src, args.seed, "k")
-    v = G.make_features(w, g.n_src, args.seed, "v")
-    log(f"[bench] {args.workload}: N={N} E={E} H={H} D={D} {w.dtype}; inputs generated in "
+    log(f"[bench] {args.workload} x {B}: N={N} E={E} H={H} D={D} {w.dtype}; inputs generated in "
         f"{time.perf_counter() - t0:.1f} s")
 
     dev = torch.device("cuda:0")
@@ -305,7 +310,20 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    rp, col = to_dev(g.row_ptr), to_dev(g.col_idx)
+    batch_build_ms = None
+    if B == 1:
+        rp, col = to_dev(g.row_ptr), to_dev(g.col_idx)
+    else:
+        # the batch is assembled on the device from the graphs' own arrays (block-diagonal CSR)
+        arrays = [to_dev(a) for a in G.batch_arrays(graphs)]
+        gat.gat_batch_csr(*arrays)
+        a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record()
+        rp, col = gat.gat_batch_csr(*arrays)
+        b0.record()
+        torch.cuda.synchronize()
+        batch_build_ms = a0.elapsed_time(b0)
     dst = to_dev(G.row_of_edge(g.row_ptr))
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     scores = torch.empty((E, H), dtype=torch.float32, device=dev)
@@ -364,7 +382,26 @@ def main():
              # the destination rows repeat along each CSR row and stay in cache: gathered k rows only
              "sddmm_k_gather_gbs": (8 * E + E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
              "kernel_source_sha256": kernel_source_digest()}
+    if batch_build_ms is not None:
+        extra["batch_graphs"] = B
+        extra["batch_build_ms"] = batch_build_ms
     if E * H < (1 << 22):
+        # launch-bound sizes: the whole step captured once in a HIP graph, 100 replays timed as one
+        graph = torch.cuda.CUDAGraph()
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(100):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        extra["step_graph_replay_us"] = a.elapsed_time(b) * 10.0   # ms for 100 replays -> us per replay
+        extra["step_graph_replay_edge_heads_per_s"] = E * H / (a.elapsed_time(b) * 1e-5)
         # launch-bound sizes: 1000 back-to-back planned fused calls timed as one interval
         plan = gat.gat_plan_build(rp, E, H, D, ws=ws)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -423,8 +460,8 @@ def main():
         "metric": METRIC, "value": value, "unit": "edge-heads/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.description, "n_rows": N, "n_edges": E, "heads": H, "head_dim": D,
-                   "features": w.dtype, "seed": args.seed,
+        "config": {"workload": w.description if B == 1 else f"{B} graphs of: {w.description}", "n_rows": N,
+                   "n_edges": E, "heads": H, "head_dim": D, "features": w.dtype, "seed": args.seed, "batch": B,
                    "step": "plan (degree binning) + sddmm q.k + fused softmax/aggregate of v"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

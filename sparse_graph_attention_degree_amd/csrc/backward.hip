@@ -313,7 +313,8 @@ __global__ __launch_bounds__(kBlock) void edge_dot_kernel(const int32_t* __restr
 // ------------------------------------------------------------------------------ softmax backward
 // out[e,h] = scale * alpha[e,h] * (g[e,h] - sum_{e' in row} alpha[e',h] * g[e',h]); out may alias g.
 constexpr int kSbG = 32;                  // lanes per row slot: lane q reads edge q/H, head q%H
-constexpr int kSbRowsPerWave = 32;
+constexpr int kSbRowsPerWave = 32;        // at most; a multiple of the 2 slots per wave
+constexpr int64_t kSbFillWaves = 2048;
 
 // rows with deg <= hi (all rows when there is no plan), a 32-lane slot per row: one pass for the
 // per-head dot, one for the output
@@ -321,16 +322,16 @@ template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_bwd_short_kernel(const int32_t* __restrict__ row_ptr,
                                                                    int64_t n_rows, const float* alpha,
                                                                    const float* grad, float* out, int hi,
-                                                                   float scale) {
+                                                                   float scale, int rpw) {
     constexpr int SC = kSbG / H;
     const int lane = lane_id();
-    const int64_t wb = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * kSbRowsPerWave;
+    const int64_t wb = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * rpw;
     if (wb >= n_rows) return;
     int rpv = 0;
-    if (lane <= kSbRowsPerWave && wb + lane <= n_rows) rpv = row_ptr[wb + lane];
+    if (lane <= rpw && wb + lane <= n_rows) rpv = row_ptr[wb + lane];
     const int q = lane % kSbG, g = lane / kSbG, es = q / H;
 #pragma unroll 1
-    for (int it = 0; it < kSbRowsPerWave / (kWave / kSbG); ++it) {
+    for (int it = 0; it < rpw / (kWave / kSbG); ++it) {
         const int j = it * (kWave / kSbG) + g;
         int e0 = shfl(rpv, j), e1 = shfl(rpv, j + 1);
         if (!(wb + j < n_rows && e1 - e0 <= hi)) e1 = e0;
@@ -493,10 +494,15 @@ hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows
             hipLaunchKernelGGL(softmax_bwd_segment_kernel<HH>,
                                dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
                                alpha, grad, out, *plan, scale);
-        const int64_t waves = (n_rows + kSbRowsPerWave - 1) / kSbRowsPerWave;
+        // rows per wave: a multiple of the slots per wave, small enough to fill the device
+        constexpr int slots = kWave / kSbG;
+        int64_t rpw = (n_rows + kSbFillWaves - 1) / kSbFillWaves;
+        rpw = (rpw + slots - 1) / slots * slots;
+        rpw = rpw < slots ? slots : (rpw > kSbRowsPerWave ? kSbRowsPerWave : rpw);
+        const int64_t waves = (n_rows + rpw - 1) / rpw;
         hipLaunchKernelGGL(softmax_bwd_short_kernel<HH>, dim3(grid_for(waves, kWavesPerBlock, INT32_MAX)),
                            dim3(kBlock), 0, stream, row_ptr, n_rows, alpha, grad, out,
-                           plan ? plan->short_max : INT32_MAX, scale);
+                           plan ? plan->short_max : INT32_MAX, scale, (int)rpw);
         if (plan)
             hipLaunchKernelGGL(softmax_bwd_hub_kernel<HH>,
                                dim3(grid_for(plan->hubseg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,

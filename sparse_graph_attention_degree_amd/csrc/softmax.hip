@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kBlock) void softmax_short_kernel(const int32_t* __
     }
 }
 
-constexpr int kBlkRows = 64;       // rows per wave
+constexpr int kBlkRows = 64;       // rows per wave (at most: fewer on graphs too small to fill the device)
+constexpr int64_t kSmFillWaves = 2048;
 constexpr int kBlkBudget = 2048;   // floats staged per wave (8 KB)
 
 // Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per 64 consecutive rows, groups of
@@ -91,13 +92,13 @@ constexpr int kBlkBudget = 2048;   // floats staged per wave (8 KB)
 // group, since its scores sit between the groups' runs.
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __restrict__ row_ptr, int64_t n_rows,
-                                                               const float* sc, float* out, int hi) {
+                                                               const float* sc, float* out, int hi, int rpw) {
     __shared__ float stage_all[kWavesPerBlock][kBlkBudget];
     float* stage = stage_all[threadIdx.x / kWave];
     const int lane = lane_id();
-    const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * kBlkRows;
+    const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * rpw;
     if (r0 >= n_rows) return;
-    const int nr = (int)((n_rows - r0) < kBlkRows ? (n_rows - r0) : kBlkRows);
+    const int nr = (int)((n_rows - r0) < rpw ? (n_rows - r0) : rpw);
     int rb = 0, re = 0;
     if (lane < nr) {
         rb = row_ptr[r0 + lane];
@@ -339,9 +340,11 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         if (plan)
             hipLaunchKernelGGL(softmax_segment_kernel<HH>, dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)),
                                dim3(kBlock), 0, stream, scores, out, *plan);
-        const int64_t bwaves = (n_rows + kBlkRows - 1) / kBlkRows;
+        int64_t rpw = (n_rows + kSmFillWaves - 1) / kSmFillWaves;   // enough waves to fill the device
+        rpw = rpw < 1 ? 1 : (rpw > kBlkRows ? kBlkRows : rpw);
+        const int64_t bwaves = (n_rows + rpw - 1) / rpw;
         hipLaunchKernelGGL(softmax_block_kernel<HH>, dim3(grid_for(bwaves, kWavesPerBlock, INT32_MAX)), dim3(kBlock),
-                           0, stream, row_ptr, n_rows, scores, out, staged);
+                           0, stream, row_ptr, n_rows, scores, out, staged, (int)rpw);
         if (short_max > staged) {
             const int64_t waves = (n_rows + kSmRowsPerWave - 1) / kSmRowsPerWave;
             hipLaunchKernelGGL(softmax_short_kernel<HH>, dim3(grid_for(waves, kWavesPerBlock, INT32_MAX)),

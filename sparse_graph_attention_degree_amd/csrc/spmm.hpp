@@ -369,15 +369,18 @@ struct Engine {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Short rows: a wave takes kRowsPerWave consecutive rows and each slot a contiguous block of
-// RS = kRowsPerWave / P of them, so a slot's edges form one contiguous run that it walks as a
-// single chunk stream (prefetching across row boundaries).  Rows with deg > short_max belong
-// to the segment kernel and are skipped; short_max = INT_MAX without a plan.
+// Short rows: a wave takes P*RS consecutive rows and each slot a contiguous block of RS of
+// them, so a slot's edges form one contiguous run that it walks as a single chunk stream
+// (prefetching across row boundaries).  RS is kRowsPerWave / P, or 1 on graphs too small to
+// give kFillWaves waves that many rows each (the grid then has one row per slot).  Rows with
+// deg > short_max belong to the segment kernel and are skipped; short_max = INT_MAX without a
+// plan.
 constexpr int kRowsPerWave = 32;
+constexpr int64_t kFillWaves = 2048;   // 256 CUs x 8 waves
 // Slot width of the short-row kernel (lanes per row in flight).
 constexpr int kShortSlotLanes = 32;
 
-template <typename T, int H, int D, int MODE, class TAB, int GMAX>
+template <typename T, int H, int D, int MODE, class TAB, int GMAX, int RS>
 __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __restrict__ row_ptr,
                                                             const int32_t* __restrict__ col, int64_t n_rows,
                                                             int64_t n_src, const float* __restrict__ sc,
@@ -386,11 +389,10 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
                                                             float* __restrict__ out, int short_max) {
     using E = Engine<T, H, D, MODE, TAB, GMAX>;
     constexpr int P = E::P, G = E::G, HD = E::HD, SC = E::SC, NV = E::NV, SM = E::SM, CM = E::CM;
-    constexpr int RS = kRowsPerWave / P;   // rows per slot (<= G/2)
     static_assert(RS + 1 <= G, "a slot holds its rows' row_ptr entries");
     const int lane = lane_id();
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    const int64_t wb = wave * kRowsPerWave;
+    const int64_t wb = wave * P * RS;
     if (wb >= n_rows) return;
     __shared__ __align__(16) float stage[kWavesPerBlock * P * E::kStage];
     const TAB vt(vf, n_src);
@@ -643,7 +645,12 @@ hipError_t launch_spmm_mode(int dtype, int H, int D, const int32_t* row_ptr, con
         const T* qt = static_cast<const T*>(q);
         const T* kt = static_cast<const T*>(k);
         const T* vt = static_cast<const T*>(v);
-        const int64_t waves = (n_rows + kRowsPerWave - 1) / kRowsPerWave;
+        // rows per slot: kRowsPerWave / P when that still gives kFillWaves waves, else 1
+        constexpr int P = Geo<T, HH, DD, kShortSlotLanes>::P;
+        constexpr int RS_MAX = kRowsPerWave / P;
+        const bool small = n_rows < kFillWaves * kRowsPerWave;
+        const int64_t rpw = small ? P : kRowsPerWave;
+        const int64_t waves = (n_rows + rpw - 1) / rpw;
         const unsigned blocks = grid_for(waves, kWavesPerBlock, INT32_MAX);
         const int short_max = plan ? plan->short_max : INT32_MAX;
         auto go = [&](auto tab_tag) {
@@ -652,9 +659,14 @@ hipError_t launch_spmm_mode(int dtype, int H, int D, const int32_t* row_ptr, con
                 hipLaunchKernelGGL((spmm_segment_kernel<T, HH, DD, MODE, TAB>),
                                    dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0,
                                    stream, col, n_src, sc, qt, kt, vt, scale, out, *plan);
-            hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB, kShortSlotLanes>), dim3(blocks),
-                               dim3(kBlock), 0, stream,
-                               row_ptr, col, n_rows, n_src, sc, qt, kt, vt, scale, out, short_max);
+            if (small)
+                hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB, kShortSlotLanes, 1>), dim3(blocks),
+                                   dim3(kBlock), 0, stream, row_ptr, col, n_rows, n_src, sc, qt, kt, vt, scale, out,
+                                   short_max);
+            else
+                hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB, kShortSlotLanes, RS_MAX>), dim3(blocks),
+                                   dim3(kBlock), 0, stream, row_ptr, col, n_rows, n_src, sc, qt, kt, vt, scale, out,
+                                   short_max);
         };
         // gathered tables below 4 GiB are read with 32-bit buffer offsets
         if (n_src * (int64_t)RB <= (int64_t)UINT32_MAX) go(TypeTag<Tab32<RB>>{});
