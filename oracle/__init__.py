@@ -68,9 +68,11 @@ class Oracle:
         L.oracle_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
         L.oracle_softmax_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
         L.oracle_layer_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp]
+        L.oracle_relation_attention.argtypes = [i64, i64, i32, i32, i32] + [vp] * 5 + [dbl] + [vp] * 8 + [vp]
         for f in (L.oracle_sddmm, L.oracle_edge_softmax, L.oracle_aggregate,
                   L.oracle_softmax_aggregate, L.oracle_layer, L.oracle_edge_softmax_backward,
-                  L.oracle_aggregate_backward, L.oracle_softmax_aggregate_backward, L.oracle_layer_backward):
+                  L.oracle_aggregate_backward, L.oracle_softmax_aggregate_backward, L.oracle_layer_backward,
+                  L.oracle_relation_attention):
             f.restype = i32
 
     def num_threads(self) -> int:
@@ -209,6 +211,26 @@ class Oracle:
                                             _dtype_code(v), float(scale), _p(grad), _p(dq), _p(dk), _p(dv))
         assert rc == 0
         return dq, dk, dv
+
+
+    # --- dense relation-biased attention block ------------------------------------------
+    def relation_attention(self, nodes, pair, mask, params: dict, eps: float = 1e-5) -> np.ndarray:
+        """out [B,N,D] of the block; params: gamma, beta [D], wq, wk, wv, wo [D,D], w1 [P,P], b1 [P],
+        w2 [H,P], b2 [H] (any float arrays, widened to double)."""
+        f = lambda a: np.ascontiguousarray(a, np.float64)  # noqa: E731
+        nodes, pair, mask = f(nodes), f(pair), f(mask)
+        B, N, D = nodes.shape
+        P = pair.shape[-1]
+        H = params["w2"].shape[0]
+        assert pair.shape == (B, N, N, P) and mask.shape == (B, N, N) and D % H == 0
+        w = {k: f(v) for k, v in params.items()}
+        out = np.full((B, N, D), np.nan, np.float64)
+        rc = self.lib.oracle_relation_attention(B, N, D, H, P, _p(nodes), _p(pair), _p(mask), _p(w["gamma"]),
+                                                _p(w["beta"]), float(eps), _p(w["wq"]), _p(w["wk"]), _p(w["wv"]),
+                                                _p(w["wo"]), _p(w["w1"]), _p(w["b1"]), _p(w["w2"]), _p(w["b2"]),
+                                                _p(out))
+        assert rc == 0
+        return out
 
 
 _default = None

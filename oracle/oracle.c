@@ -353,3 +353,107 @@ int oracle_layer_backward(int64_t n_rows, const int32_t* row_ptr, const int32_t*
     free(gs);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Dense relation-biased attention block (l2_p4, the reference-model passage): for each batch
+ * element b, with nodes x [N,D], pair features f [N,N,P] and an edge mask [N,N]:
+ *   xn  = LayerNorm(x) over D: (x - mean) / sqrt(var + eps) * gamma + beta   (biased variance)
+ *   q, k, v = xn Wq^T, xn Wk^T, xn Wv^T          (nn.Linear without bias; W is [out, in])
+ *   bias[h,i,j] = (W2 silu(W1 f[i,j] + b1) + b2)[h],  silu(t) = t / (1 + exp(-t))
+ *   logit[h,i,j] = <q_i, k_j>_h / sqrt(D/H) + bias[h,i,j]   over head h's D/H columns,
+ *                  -inf where mask[i,j] < 0.5
+ *   a[h,i,:] = softmax_j(logit[h,i,:]);  a row whose entries are all masked is all zeros
+ *   o[i, h-block] = sum_j a[h,i,j] v_j[h-block]
+ *   out = x + o Wo^T                              (residual on the un-normalised nodes)
+ * All arrays double, row-major: nodes/out [B,N,D], pair [B,N,N,P], mask [B,N,N], gamma/beta [D],
+ * wq/wk/wv/wo [D,D], w1 [P,P], b1 [P], w2 [H,P], b2 [H].
+ * ------------------------------------------------------------------------------------------ */
+int oracle_relation_attention(int64_t B, int64_t N, int D, int H, int P, const double* nodes,
+                              const double* pair, const double* mask, const double* gamma,
+                              const double* beta, double eps, const double* wq, const double* wk,
+                              const double* wv, const double* wo, const double* w1, const double* b1,
+                              const double* w2, const double* b2, double* out)
+{
+    int hd = D / H;
+    double scale = 1.0 / sqrt((double)hd);
+    size_t nd = (size_t)(N > 0 ? N : 1) * D;
+    for (int64_t b = 0; b < B; ++b) {
+        const double* x = nodes + b * N * D;
+        double* xn = (double*)malloc(nd * sizeof(double));
+        double* q = (double*)malloc(nd * sizeof(double));
+        double* k = (double*)malloc(nd * sizeof(double));
+        double* v = (double*)malloc(nd * sizeof(double));
+        double* o = (double*)malloc(nd * sizeof(double));
+        double* lg = (double*)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double* hid = (double*)malloc((size_t)P * sizeof(double));
+        if (!xn || !q || !k || !v || !o || !lg || !hid) {
+            free(xn); free(q); free(k); free(v); free(o); free(lg); free(hid);
+            return 1;
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            double mean = 0.0, var = 0.0;
+            for (int d = 0; d < D; ++d) mean += x[i * D + d];
+            mean /= D;
+            for (int d = 0; d < D; ++d) var += (x[i * D + d] - mean) * (x[i * D + d] - mean);
+            var /= D;
+            for (int d = 0; d < D; ++d)
+                xn[i * D + d] = (x[i * D + d] - mean) / sqrt(var + eps) * gamma[d] + beta[d];
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            for (int r = 0; r < D; ++r) {
+                double sq = 0.0, sk = 0.0, sv = 0.0;
+                for (int c = 0; c < D; ++c) {
+                    sq += xn[i * D + c] * wq[r * D + c];
+                    sk += xn[i * D + c] * wk[r * D + c];
+                    sv += xn[i * D + c] * wv[r * D + c];
+                }
+                q[i * D + r] = sq;
+                k[i * D + r] = sk;
+                v[i * D + r] = sv;
+            }
+        }
+        for (int h = 0; h < H; ++h) {
+            for (int64_t i = 0; i < N; ++i) {
+                int any = 0;
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < N; ++j) {
+                    lg[j] = -INFINITY;
+                    if (mask[(b * N + i) * N + j] < 0.5) continue;
+                    const double* f = pair + ((b * N + i) * N + j) * P;
+                    double rb = b2[h];
+                    for (int p = 0; p < P; ++p) {
+                        double t = b1[p];
+                        for (int c = 0; c < P; ++c) t += w1[p * P + c] * f[c];
+                        hid[p] = t / (1.0 + exp(-t));
+                    }
+                    for (int p = 0; p < P; ++p) rb += w2[h * P + p] * hid[p];
+                    double dot = 0.0;
+                    for (int t = 0; t < hd; ++t) dot += q[i * D + h * hd + t] * k[j * D + h * hd + t];
+                    lg[j] = dot * scale + rb;
+                    any = 1;
+                    if (lg[j] > mx) mx = lg[j];
+                }
+                double z = 0.0;
+                if (any)
+                    for (int64_t j = 0; j < N; ++j)
+                        if (lg[j] != -INFINITY) z += exp(lg[j] - mx);
+                for (int t = 0; t < hd; ++t) {
+                    double acc = 0.0;
+                    if (any)
+                        for (int64_t j = 0; j < N; ++j)
+                            if (lg[j] != -INFINITY) acc += exp(lg[j] - mx) / z * v[j * D + h * hd + t];
+                    o[i * D + h * hd + t] = acc;
+                }
+            }
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            for (int r = 0; r < D; ++r) {
+                double s = 0.0;
+                for (int c = 0; c < D; ++c) s += o[i * D + c] * wo[r * D + c];
+                out[(b * N + i) * D + r] = x[i * D + r] + s;
+            }
+        }
+        free(xn); free(q); free(k); free(v); free(o); free(lg); free(hid);
+    }
+    return 0;
+}

@@ -336,6 +336,36 @@ def take_rows(g: CsrGraph, rows: np.ndarray):
     return sub_rp.astype(np.int32), g.col_idx[edge_ids], edge_ids
 
 
+# Dense relation-biased attention block (the l2_p4 page): its shapes, and seeded inputs with
+# nn.Linear-style weights U(-1/sqrt(fan_in), 1/sqrt(fan_in)) and a LayerNorm affine near identity.
+RELATION_BLOCK = dict(B=4, N=24, D=96, P=16, H=4)
+
+
+def make_relation_block(B: int, N: int, D: int, H: int, P: int, seed: int = 0, mask: str = "ones"):
+    """(nodes [B,N,D], pair [B,N,N,P], mask [B,N,N], params) as float32.  mask: "ones" (every pair
+    attends, as the page's inputs), "random" (Bernoulli(0.6) with the diagonal kept), or
+    "random_empty" (Bernoulli(0.4), some rows with no pair at all)."""
+    r = np.random.default_rng(np.random.SeedSequence([seed, 0x5E1A]))
+    f32 = lambda a: np.asarray(a, np.float32)  # noqa: E731
+    nodes = f32(r.standard_normal((B, N, D)))
+    pair = f32(r.standard_normal((B, N, N, P)))
+    if mask == "ones":
+        m = np.ones((B, N, N), np.float32)
+    elif mask == "random":
+        m = f32(r.random((B, N, N)) < 0.6)
+        m[:, np.arange(N), np.arange(N)] = 1.0
+    elif mask == "random_empty":
+        m = f32(r.random((B, N, N)) < 0.4)
+        m[:, ::3, :] = 0.0
+    else:
+        raise ValueError(mask)
+    u = lambda shape, fan_in: f32(r.uniform(-1.0, 1.0, shape) / np.sqrt(fan_in))  # noqa: E731
+    params = dict(gamma=f32(1.0 + 0.1 * r.standard_normal(D)), beta=f32(0.1 * r.standard_normal(D)),
+                  wq=u((D, D), D), wk=u((D, D), D), wv=u((D, D), D), wo=u((D, D), D),
+                  w1=u((P, P), P), b1=u((P,), P), w2=u((H, P), P), b2=u((H,), P))
+    return nodes, pair, m, params
+
+
 def batch_arrays(graphs):
     """The inputs of a block-diagonal batch: the graphs' row_ptr and col_idx concatenated as they
     are, and int32 prefix sums [B+1] of their rows, edges and sources."""

@@ -399,11 +399,66 @@ def pin_aggregate_backward_integer_exact(orc):
         assert np.array_equal(dX[:, h, :], (Wd.T @ Gi[:, h, :]).astype(np.float64))
 
 
+# ------------------------------------------------------------------------------- dense relation block
+def _torch_relation_block(nodes, pair, mask, prm, eps=1e-5):
+    """torch (fp64, CPU) modules of the block: LayerNorm, bias-free q/k/v/out Linear layers, the
+    Linear-SiLU-Linear pair MLP, masked softmax, residual."""
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.tensor(np.asarray(a, np.float64))  # noqa: E731
+    x, f, m = t(nodes), t(pair), t(mask)
+    B, N, D = x.shape
+    H = prm["w2"].shape[0]
+    hd = D // H
+    xn = F.layer_norm(x, (D,), t(prm["gamma"]), t(prm["beta"]), eps)
+    q, k, v = (F.linear(xn, t(prm[n])).view(B, N, H, hd).transpose(1, 2) for n in ("wq", "wk", "wv"))
+    bias = F.linear(F.silu(F.linear(f, t(prm["w1"]), t(prm["b1"]))), t(prm["w2"]), t(prm["b2"])).permute(0, 3, 1, 2)
+    logits = (q @ k.transpose(-1, -2)) / np.sqrt(hd) + bias
+    logits = logits.masked_fill(m.unsqueeze(1) < 0.5, float("-inf"))
+    a = torch.softmax(logits, dim=-1)
+    o = (a @ v).transpose(1, 2).reshape(B, N, D)
+    return (x + F.linear(o, t(prm["wo"]))).numpy()
+
+
+def pin_relation_attention_torch(orc):
+    """The block against torch's own modules, for the page's shapes and others, every row attending."""
+    for seed, (B, N, D, H, P), mk in [(41, (4, 24, 96, 4, 16), "ones"), (42, (2, 7, 32, 2, 8), "random"),
+                                     (43, (1, 1, 16, 1, 4), "ones"), (44, (3, 33, 64, 8, 5), "random")]:
+        nodes, pair, mask, prm = G.make_relation_block(B, N, D, H, P, seed, mask=mk)
+        got = orc.relation_attention(nodes, pair, mask, prm)
+        np.testing.assert_allclose(got, _torch_relation_block(nodes, pair, mask, prm), rtol=1e-11, atol=1e-12)
+
+
+def pin_relation_attention_closed_forms(orc):
+    """A row with no pair kept returns its node row exactly; with one pair kept per row the result
+    does not depend on q, k or the pair MLP; a constant added to a head's MLP bias changes nothing;
+    relabelling the nodes permutes the output."""
+    B, N, D, H, P = 2, 9, 32, 4, 6
+    nodes, pair, mask, prm = G.make_relation_block(B, N, D, H, P, 45, mask="random_empty")
+    out = orc.relation_attention(nodes, pair, mask, prm)
+    empty = mask.sum(-1) == 0
+    assert empty.any()
+    assert np.array_equal(out[empty], nodes[empty].astype(np.float64))
+    one = np.zeros((B, N, N), np.float32)
+    one[:, np.arange(N), (np.arange(N) * 5 + 2) % N] = 1.0
+    base = orc.relation_attention(nodes, pair, one, prm)
+    alt = dict(prm, wq=prm["wk"] * 3.0, wk=-prm["wq"], w1=prm["w1"][::-1].copy(), b2=prm["b2"] + 7.0)
+    assert np.array_equal(orc.relation_attention(nodes, pair, one, alt), base)
+    full = np.ones((B, N, N), np.float32)
+    ref = orc.relation_attention(nodes, pair, full, prm)
+    np.testing.assert_allclose(orc.relation_attention(nodes, pair, full, dict(prm, b2=prm["b2"] + 3.5)), ref,
+                               rtol=1e-12, atol=1e-12)
+    perm = np.random.default_rng(46).permutation(N)
+    permuted = orc.relation_attention(nodes[:, perm], pair[:, perm][:, :, perm], mask[:, perm][:, :, perm], prm)
+    np.testing.assert_allclose(permuted, out[:, perm], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [pin_sddmm_dense, pin_sddmm_integer_exact, pin_softmax_closed_forms, pin_softmax_dense,
             pin_softmax_invariants, pin_aggregate_dense, pin_aggregate_integer_exact,
             pin_zero_rows_positive_zero, pin_softmax_aggregate_dense, pin_softmax_aggregate_closed_forms,
             pin_layer_dense, pin_backward_finite_differences, pin_layer_backward_autograd,
-            pin_backward_invariants, pin_aggregate_backward_integer_exact]
+            pin_backward_invariants, pin_aggregate_backward_integer_exact, pin_relation_attention_torch,
+            pin_relation_attention_closed_forms]
 
 
 def run_all(orc) -> list:

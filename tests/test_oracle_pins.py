@@ -67,6 +67,16 @@ MUTANTS = [
     ("layer_bwd_dv_weights_are_scores", "n_src, a, v, dtype, grad, ga, dv);", "n_src, s, v, dtype, grad, ga, dv);"),
     ("softagg_bwd_weights_are_scores", "n_src, alpha, feat, dtype, grad, ga, dfeat);",
      "n_src, scores, feat, dtype, grad, ga, dfeat);"),
+    # dense relation-biased attention block
+    ("relblock_unbiased_variance", "var /= D;", "var /= (D - 1);"),
+    ("relblock_eps_dropped", "/ sqrt(var + eps) * gamma[d]", "/ sqrt(var) * gamma[d]"),
+    ("relblock_weight_transposed", "sq += xn[i * D + c] * wq[r * D + c];", "sq += xn[i * D + c] * wq[c * D + r];"),
+    ("relblock_silu_dropped", "hid[p] = t / (1.0 + exp(-t));", "hid[p] = t;"),
+    ("relblock_scale_dropped", "lg[j] = dot * scale + rb;", "lg[j] = dot + rb;"),
+    ("relblock_mask_inverted", "if (mask[(b * N + i) * N + j] < 0.5) continue;",
+     "if (mask[(b * N + i) * N + j] > 0.5) continue;"),
+    ("relblock_residual_dropped", "out[(b * N + i) * D + r] = x[i * D + r] + s;", "out[(b * N + i) * D + r] = s;"),
+    ("relblock_bias_head0", "rb += w2[h * P + p] * hid[p];", "rb += w2[p] * hid[p];"),
 ]
 
 
