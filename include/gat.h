@@ -198,6 +198,30 @@ gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col,
                          const int32_t* edge_off, const int32_t* src_off, int64_t n_graphs, int64_t n_rows,
                          int64_t n_edges, int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
 
+/*
+ * Dense relation-biased attention block [l2_p4] (reference-model passage), for each of `batch`
+ * elements with nodes x [n_nodes,dim], pair features f [n_nodes,n_nodes,pair_dim] and an edge
+ * mask [n_nodes,n_nodes]:
+ *   xn = LayerNorm(x) over dim: (x - mean) / sqrt(var + eps) * gamma + beta  (biased variance)
+ *   q, k, v = xn Wq^T, xn Wk^T, xn Wv^T;  bias[h,i,j] = (W2 silu(W1 f[i,j] + b1) + b2)[h]
+ *   logit[h,i,j] = <q_i, k_j>_h / sqrt(dim/heads) + bias[h,i,j], -inf where mask[i,j] < 0.5
+ *   a = softmax_j(logit) (a row with every pair masked is all zeros; PyTorch would give NaN)
+ *   out = x + (sum_j a[h,i,j] v_j per head, concatenated) Wo^T
+ * fp32, row-major: nodes/out [batch,n_nodes,dim], pair_feats [batch,n_nodes,n_nodes,pair_dim],
+ * edge_mask [batch,n_nodes,n_nodes], gamma/beta [dim], wq/wk/wv/wo [dim,dim] ([out,in], as
+ * nn.Linear stores them), w1 [pair_dim,pair_dim], b1 [pair_dim], w2 [heads,pair_dim], b2 [heads].
+ * nodes, the four dim x dim weights and out must be 16-byte aligned; out may equal nodes.
+ * Supported: dim a multiple of 4 and of heads, heads <= 16, and the per-element working set
+ * (4*n_nodes*dim + heads*n_nodes^2 floats) within the 160 KB of LDS of one workgroup
+ * (gat_relation_block_lds_bytes returns 0 otherwise).  One workgroup per batch element.
+ */
+size_t gat_relation_block_lds_bytes(int n_nodes, int dim, int heads, int pair_dim);
+gat_status gat_relation_block(const float* nodes, const float* pair_feats, const float* edge_mask,
+                              const float* gamma, const float* beta, float eps, const float* wq,
+                              const float* wk, const float* wv, const float* wo, const float* w1,
+                              const float* b1, const float* w2, const float* b2, int64_t batch,
+                              int n_nodes, int dim, int heads, int pair_dim, float* out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Backward.  No page writes the backward pass out; the l1_p10 page (edge-only SDDMM, the
  * passage on the backward pass) notes that gradients sum into the feature rows that edges read.

@@ -353,6 +353,31 @@ gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col,
                                             n_edges, row_ptr, col_idx, stream));
 }
 
+size_t gat_relation_block_lds_bytes(int n_nodes, int dim, int heads, int pair_dim) {
+    if (n_nodes < 0 || dim <= 0 || heads <= 0 || heads > gat::kRbMaxHeads || dim % heads != 0 || dim % 4 != 0 ||
+        pair_dim <= 0 || pair_dim > 1024)
+        return 0;
+    const size_t b = gat::relation_block_lds_bytes(n_nodes, dim, heads);
+    return b <= gat::kRbMaxLds ? (b > 0 ? b : 1) : 0;
+}
+
+gat_status gat_relation_block(const float* nodes, const float* pair_feats, const float* edge_mask, const float* gamma,
+                              const float* beta, float eps, const float* wq, const float* wk, const float* wv,
+                              const float* wo, const float* w1, const float* b1, const float* w2, const float* b2,
+                              int64_t batch, int n_nodes, int dim, int heads, int pair_dim, float* out,
+                              hipStream_t stream) {
+    if (batch < 0 || batch > kMaxIndex || n_nodes < 0 || n_nodes > 4096) return GAT_ERR_SIZE;
+    if (gat_relation_block_lds_bytes(n_nodes, dim, heads, pair_dim) == 0) return GAT_ERR_UNSUPPORTED;
+    if (batch == 0 || n_nodes == 0) return GAT_OK;
+    if (!nodes || !pair_feats || !edge_mask || !gamma || !beta || !wq || !wk || !wv || !wo || !w1 || !b1 || !w2 ||
+        !b2 || !out)
+        return GAT_ERR_NULL;
+    for (const float* p : {nodes, wq, wk, wv, wo, static_cast<const float*>(out)})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return GAT_ERR_ARGS;   // 16-byte row loads
+    return hip_status(gat::launch_relation_block(nodes, pair_feats, edge_mask, gamma, beta, eps, wq, wk, wv, wo, w1,
+                                                 b1, w2, b2, batch, n_nodes, dim, heads, pair_dim, out, stream));
+}
+
 // ------------------------------------------------------------------------------ backward
 size_t gat_csc_sizeof(void) { return sizeof(gat_csc); }
 

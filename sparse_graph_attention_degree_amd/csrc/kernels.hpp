@@ -132,6 +132,15 @@ hipError_t launch_batch_csr(const int32_t* local_row_ptr, const int32_t* local_c
                             const int32_t* edge_off, const int32_t* src_off, int64_t n_graphs, int64_t n_rows,
                             int64_t n_edges, int32_t* row_ptr, int32_t* col, hipStream_t stream);
 
+// dense relation-biased attention block: one workgroup per batch element, everything in LDS
+constexpr size_t kRbMaxLds = 160 * 1024;   // gfx950 LDS per workgroup
+constexpr int kRbMaxHeads = 16;
+size_t relation_block_lds_bytes(int N, int D, int H);
+hipError_t launch_relation_block(const float* nodes, const float* pair, const float* mask, const float* gamma,
+                                 const float* beta, float eps, const float* wq, const float* wk, const float* wv,
+                                 const float* wo, const float* w1, const float* b1, const float* w2, const float* b2,
+                                 int64_t B, int N, int D, int H, int P, float* out, hipStream_t stream);
+
 // Rows per binner block (256 threads x 4 consecutive rows).
 constexpr int kPlanRowsPerThread = 4;
 constexpr int kPlanRowsPerBlock = kBlock * kPlanRowsPerThread;

@@ -26,7 +26,7 @@ EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge
             "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof",
             "gat_csc_workspace_bytes", "gat_csc_sizeof", "gat_csc_build", "gat_edge_softmax_backward",
             "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward",
-            "gat_batch_csr"]
+            "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block"]
 
 
 class GatError(RuntimeError):
@@ -88,9 +88,12 @@ def _lib():
     L.gat_fused_layer_backward.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp,
                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.gat_batch_csr.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    L.gat_relation_block_lds_bytes.argtypes = [i32, i32, i32, i32]
+    L.gat_relation_block_lds_bytes.restype = sz
+    L.gat_relation_block.argtypes = [vp, vp, vp, vp, vp, f32] + [vp] * 8 + [i64, i32, i32, i32, i32, vp, vp]
     for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer,
               L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward,
-              L.gat_batch_csr):
+              L.gat_batch_csr, L.gat_relation_block):
         f.restype = i32
     L.gat_status_str.argtypes = [i32]
     L.gat_status_str.restype = ctypes.c_char_p
@@ -404,3 +407,27 @@ def gat_batch_csr(local_row_ptr, local_col, row_off, edge_off, src_off, stream=N
                                                  _ptr(edge_off), _ptr(src_off), B, n_rows, n_edges, _ptr(row_ptr),
                                                  _ptr(col), _stream(stream)))
     return row_ptr, col
+
+
+# ----------------------------------------------------------------------------- dense relation block
+def gat_relation_block(nodes, pair_feats, edge_mask, params: dict, eps: float = 1e-5, out=None, stream=None):
+    """The l2_p4 block: nodes fp32 [B,N,D], pair_feats [B,N,N,P], edge_mask [B,N,N]; params: gamma,
+    beta [D], wq, wk, wv, wo [D,D], w1 [P,P], b1 [P], w2 [H,P], b2 [H] (device fp32 tensors)."""
+    _dev(nodes, "nodes", torch.float32, 3)
+    _dev(pair_feats, "pair_feats", torch.float32, 4)
+    _dev(edge_mask, "edge_mask", torch.float32, 3)
+    names = ("gamma", "beta", "wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2")
+    for n in names:
+        _dev(params[n], n, torch.float32)
+    B, N, D = nodes.shape
+    P = pair_feats.shape[-1]
+    H = params["w2"].shape[0]
+    if pair_feats.shape[:3] != (B, N, N) or edge_mask.shape != (B, N, N):
+        raise ValueError("inconsistent relation-block shapes")
+    if out is None:
+        out = torch.empty_like(nodes)
+    _dev(out, "out", torch.float32, 3)
+    _check("gat_relation_block", _lib().gat_relation_block(
+        _ptr(nodes), _ptr(pair_feats), _ptr(edge_mask), *(_ptr(params[n]) for n in names[:2]), float(eps),
+        *(_ptr(params[n]) for n in names[2:]), B, N, D, H, P, _ptr(out), _stream(stream)))
+    return out

@@ -237,3 +237,17 @@ def test_block_diagonal_reference():
         assert np.array_equal(bd.col_idx[eo[b]:eo[b + 1]] - so[b], g.col_idx)
         assert np.array_equal(bd.row_ptr[ro[b]:ro[b + 1] + 1] - eo[b], g.row_ptr)
         assert np.array_equal(lrp[ro[b] + b:ro[b + 1] + b + 1], g.row_ptr)
+
+
+def test_relation_block_host_checks(L):
+    f = L.gat_relation_block
+    args = lambda B, N, D, H, P, nodes=FAKE, out=FAKE: (nodes, FAKE, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, FAKE,  # noqa: E731
+                                                        FAKE, FAKE, FAKE, FAKE, B, N, D, H, P, out, None)
+    assert f(*args(-1, 24, 96, 4, 16)) == SIZE
+    assert f(*args(4, 24, 96, 5, 16)) == UNSUP
+    assert f(*args(4, 64, 128, 8, 16)) == UNSUP
+    assert f(*args(4, 24, 96, 4, 0)) == UNSUP
+    assert f(*args(4, 24, 96, 4, 16, nodes=None)) == NULL
+    assert f(*args(4, 24, 96, 4, 16, out=ctypes.c_void_p(0x1004))) == ARGS
+    assert f(*args(0, 24, 96, 4, 16, nodes=None, out=None)) == OK
+    assert L.gat_relation_block_lds_bytes(24, 96, 4, 16) == (4 * 24 * 96 + 4 * 24 * 24) * 4
