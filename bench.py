@@ -197,6 +197,64 @@ def bench_backward(gat, rp, col, qd, kd, vd, scores, N, E, H, D, feat_bytes, str
     return out
 
 
+def bench_relation(args, gat, G):
+    """The l2_p4 dense block: one call over `--batch` elements (default: the page's 4) of 24 nodes x
+    96 features, 4 heads, 16 pair features."""
+    import torch
+    sh = dict(G.RELATION_BLOCK)
+    if args.batch > 1:
+        sh["B"] = args.batch
+    B, N, D, H, P = sh["B"], sh["N"], sh["D"], sh["H"], sh["P"]
+    nodes, pair, mask, prm = G.make_relation_block(B, N, D, H, P, args.seed, mask="ones")
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    nd, pd, md = t(nodes), t(pair), t(mask)
+    pr = {k: t(v) for k, v in prm.items()}
+    out = torch.empty_like(nd)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        gat.gat_relation_block(nd, pd, md, pr, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        gat.gat_relation_block(nd, pd, md, pr, out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tk = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    # arithmetic per element: four D x D projections, pair MLP, q.k and a.v
+    flops = B * (4 * 2 * N * D * D + N * N * 2 * (P * P + P * H) + 2 * 2 * H * N * N * (D // H))
+    nbytes = B * 4 * (2 * N * D + N * N * P + N * N) + 4 * (4 * D * D + P * P + P + H * P + H + 2 * D)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        orc = oracle.get()
+        k = max(1, min(B, 4))
+        t1, reps = time.perf_counter(), 0
+        while time.perf_counter() - t1 < 3.0:
+            orc.relation_attention(nodes[:k], pair[:k], mask[:k], prm)
+            reps += 1
+        dt = (time.perf_counter() - t1) / reps
+        cpu = {"value": k / dt, "unit": "block elements/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
+               "sample": f"{k} elements, {reps} repetitions (the oracle's block is single-threaded)"}
+    print(json.dumps({
+        "metric": "dense relation-biased attention block (l2_p4): batch elements per second", "value": B / tk,
+        "unit": "block elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"relation block: {B} x {N} nodes, {D} features, {H} heads, {P} pair features",
+                   "batch": B, "seed": args.seed},
+        "roofline": {"bound": "alu", "achieved": flops / tk / 1e12, "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": flops / tk / 1e12 / 157.3, "traffic": None,
+                     "kernel": "relation_block_kernel (one workgroup per element; fp32 vector FMA)"},
+        "cpu_baseline": cpu,
+        "extra": {"t_call_us": tk * 1e6, "flops_per_call": flops, "hbm_bytes_per_call": nbytes,
+                  "hbm_gbs": nbytes / tk / 1e9},
+    }))
+
+
 def bench_coo(args, w, gat, G):
     """COO workload: one step = one SDDMM over the edge list."""
     import torch
@@ -258,7 +316,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "relation"])
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
@@ -287,6 +345,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
 
+    if args.workload == "relation":
+        bench_relation(args, gat, G)
+        return
     w = G.WORKLOADS[args.workload]
     if w.kind == "coo":
         bench_coo(args, w, gat, G)

@@ -211,8 +211,9 @@ gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col,
  * edge_mask [batch,n_nodes,n_nodes], gamma/beta [dim], wq/wk/wv/wo [dim,dim] ([out,in], as
  * nn.Linear stores them), w1 [pair_dim,pair_dim], b1 [pair_dim], w2 [heads,pair_dim], b2 [heads].
  * nodes, the four dim x dim weights and out must be 16-byte aligned; out may equal nodes.
- * Supported: dim a multiple of 4 and of heads, heads <= 16, and the per-element working set
- * (4*n_nodes*dim + heads*n_nodes^2 floats) within the 160 KB of LDS of one workgroup
+ * Supported: dim <= 256 and a multiple of 4 and of heads, heads <= 16, pair_dim <= 64, and the
+ * per-element working set (about 4*n_nodes*dim + (heads+1)*n_nodes^2 floats, the pair MLP's
+ * weights and two 16-row blocks of a weight matrix) within the 160 KB of LDS of one workgroup
  * (gat_relation_block_lds_bytes returns 0 otherwise).  One workgroup per batch element.
  */
 size_t gat_relation_block_lds_bytes(int n_nodes, int dim, int heads, int pair_dim);

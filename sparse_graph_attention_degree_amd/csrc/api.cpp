@@ -354,10 +354,10 @@ gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col,
 }
 
 size_t gat_relation_block_lds_bytes(int n_nodes, int dim, int heads, int pair_dim) {
-    if (n_nodes < 0 || dim <= 0 || heads <= 0 || heads > gat::kRbMaxHeads || dim % heads != 0 || dim % 4 != 0 ||
-        pair_dim <= 0 || pair_dim > 1024)
+    if (n_nodes < 0 || n_nodes > 4096 || dim <= 0 || dim > gat::kRbMaxDim || heads <= 0 ||
+        heads > gat::kRbMaxHeads || dim % heads != 0 || dim % 4 != 0 || pair_dim <= 0 || pair_dim > gat::kRbMaxPairDim)
         return 0;
-    const size_t b = gat::relation_block_lds_bytes(n_nodes, dim, heads);
+    const size_t b = gat::relation_block_lds_bytes(n_nodes, dim, heads, pair_dim);
     return b <= gat::kRbMaxLds ? (b > 0 ? b : 1) : 0;
 }
 

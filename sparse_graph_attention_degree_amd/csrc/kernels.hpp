@@ -135,7 +135,9 @@ hipError_t launch_batch_csr(const int32_t* local_row_ptr, const int32_t* local_c
 // dense relation-biased attention block: one workgroup per batch element, everything in LDS
 constexpr size_t kRbMaxLds = 160 * 1024;   // gfx950 LDS per workgroup
 constexpr int kRbMaxHeads = 16;
-size_t relation_block_lds_bytes(int N, int D, int H);
+size_t relation_block_lds_bytes(int N, int D, int H, int P);
+constexpr int kRbMaxPairDim = 64;
+constexpr int kRbMaxDim = 256;   // a block of 16 weight rows is at most 4 float4 loads per thread
 hipError_t launch_relation_block(const float* nodes, const float* pair, const float* mask, const float* gamma,
                                  const float* beta, float eps, const float* wq, const float* wk, const float* wv,
                                  const float* wo, const float* w1, const float* b1, const float* w2, const float* b2,

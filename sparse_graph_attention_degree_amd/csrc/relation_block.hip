@@ -6,17 +6,22 @@
 // element runs in one workgroup out of LDS -- one launch per call, no intermediate reaches HBM --
 // and many batch elements run as many workgroups.
 //
-// LDS per workgroup (floats): xn / o [N*D], q, k, v [N*D] each, logits [H*N*N] (at most
-// kRbMaxLds bytes; the C-ABI refuses larger shapes).  Steps, separated
-// by workgroup barriers:
-//  1. LayerNorm: a wave per node row, mean and variance by xor-shuffle sums over the row.
-//  2. q, k, v: a thread per output column of each projection, rows in groups of 8 held in
-//     registers while the weight row streams through (16-byte loads).
-//  3. pair bias: a thread per (i, j) pair runs the MLP in registers (masked pairs get -inf).
+// The block for one element is a chain of short dependent steps, so the design is about memory
+// latency: every small input goes to LDS in one burst at the start, and the weight matrices stream
+// through LDS in double-buffered blocks.  LDS per workgroup (floats): x / LayerNorm(x) / o [N*D],
+// q, k, v [N*(D+1)] each, logits [H*N*N], the mask [N*N], the pair MLP's weights, and two blocks of
+// weight rows (at most kRbMaxLds bytes; the C-ABI refuses larger shapes).  Steps, separated by
+// workgroup barriers:
+//  0. x, the mask and the MLP weights into LDS (all loads in flight together).
+//  1. pair bias: the pair features stream through LDS (coalesced) in rounds; a thread per (i, j)
+//     pair runs the MLP out of LDS, its SiLU outputs beside its features (masked pairs get -inf).
+//  2. LayerNorm in place: a wave per node row, mean and variance by xor-shuffle sums over the row.
+//  3. q, k, v: weight rows through LDS kRbCols at a time (coalesced 16-byte loads of the next block
+//     issued before the current one is used); a thread per output.
 //  4. logits: a thread per (h, i, j): scaled q.k over the head's columns plus the bias.
 //  5. softmax: a thread per (h, i) row; a row with every pair masked becomes all zeros.
 //  6. o = a v: a thread per (i, column).
-//  7. out = x + o Wo^T: as step 2, with the residual added at the store.
+//  7. out = x + o Wo^T: as step 2, with the residual (x re-read, L2-resident) added at the store.
 #include <math.h>
 
 #include "kernels.hpp"
@@ -25,111 +30,188 @@ namespace gat {
 
 namespace {
 
-constexpr int kRbRows = 8;   // node rows per register group in the projections
+constexpr int kRbCols = 16;   // weight rows (output columns) staged in LDS per step
 
-// y[i, r] = sum_c a[i, c] * w[r, c] for rows i < n, columns r < m (w row-major [m, kdim], global);
-// a in LDS [n, kdim]; y in LDS [n, ldy] at column offset; thread per column.
+// LDS regions in floats, each starting on a 16-byte boundary
+struct RbLayout {
+    int xn, qs, ks, vs, lg, mk, mw, wbuf, total;
+};
+
+__host__ __device__ inline RbLayout rb_layout(int N, int D, int H, int P) {
+    auto up = [](int v) { return (v + 3) & ~3; };
+    RbLayout L{};
+    int o = 0;
+    L.xn = o, o += up(N * D);
+    L.qs = o, o += up(N * (D + 1) > 2 * P + 1 ? N * (D + 1) : 2 * P + 1);   // also the pair-feature stage
+    L.ks = o, o += up(N * (D + 1));
+    L.vs = o, o += up(N * (D + 1));
+    L.lg = o, o += up(H * N * N);
+    L.mk = o, o += up(N * N);
+    L.mw = o, o += up(P * P + P + H * P + H);
+    L.wbuf = o, o += 2 * kRbCols * (D + 4);
+    L.total = o;
+    return L;
+}
+
+// y[i, r] = sum_c a[i, c] * w[r, c] for rows i < n and columns r < m.  w is row-major [m, kdim] in
+// global memory (the same for every workgroup, so L2-resident); a is LDS [n, kdim] (16-byte rows).
+// The weight rows go through LDS kRbCols at a time, double-buffered: the coalesced loads of the
+// next block are issued before the current one is used, so one memory latency overlaps one block
+// of arithmetic.  wbuf: 2 * kRbCols * (kdim + 4) floats (rows padded against bank conflicts).
 __device__ void rb_project(const float* __restrict__ a, int n, int kdim, const float* __restrict__ w, int m,
-                           float* y, int ldy) {
-    for (int r = threadIdx.x; r < m; r += kBlock) {
-        const float* wr = w + (int64_t)r * kdim;
-        for (int i0 = 0; i0 < n; i0 += kRbRows) {
-            float acc[kRbRows];
+                           float* y, int ldy, float* wbuf) {
+    const int ldw = kdim + 4;
+    const int nblk = (m + kRbCols - 1) / kRbCols;
+    const int per = kRbCols * kdim / 4;   // float4s per block
+    float4 pre[4];                         // this thread's share of the next block (<= 4 float4s)
+    auto fetch = [&](int blk) {
 #pragma unroll
-            for (int u = 0; u < kRbRows; ++u) acc[u] = 0.f;
+        for (int u = 0; u < 4; ++u) {
+            const int e = threadIdx.x + u * kBlock;
+            pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            const int r = blk * kRbCols + (4 * e) / kdim;
+            if (e < per && r < m) pre[u] = *reinterpret_cast<const float4*>(w + (int64_t)r * kdim + (4 * e) % kdim);
+        }
+    };
+    auto stash = [&](float* dst) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = threadIdx.x + u * kBlock;
+            if (e < per) *reinterpret_cast<float4*>(dst + ((4 * e) / kdim) * ldw + (4 * e) % kdim) = pre[u];
+        }
+    };
+    fetch(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        float* cur = wbuf + (blk & 1) * kRbCols * ldw;
+        stash(cur);
+        __syncthreads();
+        if (blk + 1 < nblk) fetch(blk + 1);
+        for (int o = threadIdx.x; o < n * kRbCols; o += kBlock) {
+            const int i = o / kRbCols, rr = o % kRbCols, r = blk * kRbCols + rr;
+            if (r >= m) continue;
+            const float* ar = a + i * kdim;
+            const float* wr = cur + rr * ldw;
+            float acc = 0.f;
+#pragma unroll 8
             for (int c = 0; c < kdim; c += 4) {
+                const float4 av = *reinterpret_cast<const float4*>(ar + c);
                 const float4 wv = *reinterpret_cast<const float4*>(wr + c);
-#pragma unroll
-                for (int u = 0; u < kRbRows; ++u) {
-                    if (i0 + u < n) {
-                        const float4 av = *reinterpret_cast<const float4*>(a + (i0 + u) * kdim + c);
-                        acc[u] = fmaf(av.x, wv.x, fmaf(av.y, wv.y, fmaf(av.z, wv.z, fmaf(av.w, wv.w, acc[u]))));
-                    }
-                }
+                acc = fmaf(av.x, wv.x, fmaf(av.y, wv.y, fmaf(av.z, wv.z, fmaf(av.w, wv.w, acc))));
             }
-#pragma unroll
-            for (int u = 0; u < kRbRows; ++u)
-                if (i0 + u < n) y[(i0 + u) * ldy + r] = acc[u];
+            y[i * ldy + r] = acc;
         }
     }
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(kBlock) void relation_block_kernel(
     const float* nodes, const float* __restrict__ pair, const float* __restrict__ mask,
     const float* __restrict__ gamma, const float* __restrict__ beta, float eps, const float* __restrict__ wq,
     const float* __restrict__ wk, const float* __restrict__ wv, const float* __restrict__ wo,
-    const float* __restrict__ w1, const float* __restrict__ b1,
-    const float* __restrict__ w2, const float* __restrict__ b2, int N, int D, int H, int P,
-    float* out) {
+    const float* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
+    const float* __restrict__ b2, int N, int D, int H, int P, float* out) {
     extern __shared__ __align__(16) float lds[];
     const int b = blockIdx.x;
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
-    const int ND = N * D, hd = D / H;
-    float* xn = lds;            // then o
-    float* qs = lds + ND;
-    float* ks = qs + ND;
-    float* vs = ks + ND;
-    float* lg = vs + ND;        // [H][N][N]
+    const int ND = N * D, hd = D / H, ld = D + 1;   // q/k/v rows padded by one float (bank spread)
+    const RbLayout L = rb_layout(N, D, H, P);
+    float* xn = lds + L.xn;          // [N][D]: x, then LayerNorm(x), then o
+    float* qs = lds + L.qs;          // [N][ld]
+    float* ks = lds + L.ks;
+    float* vs = lds + L.vs;
+    float* lg = lds + L.lg;          // [H][N][N]
+    float* mk = lds + L.mk;          // [N][N]
+    float* mw = lds + L.mw;          // pair MLP: w1 [P*P], b1 [P], w2 [H*P], b2 [H]
+    float* wbuf = lds + L.wbuf;      // two blocks of kRbCols weight rows
     const float* x = nodes + (int64_t)b * ND;
 
-    // 1. LayerNorm
+    // 0. everything small into LDS with all loads in flight together: x, the mask, the MLP weights
+    for (int e = t; e < ND / 4; e += kBlock)
+        reinterpret_cast<float4*>(xn)[e] = reinterpret_cast<const float4*>(x)[e];
+    const float* mb = mask + (int64_t)b * N * N;
+    for (int e = t; e < N * N; e += kBlock) mk[e] = mb[e];
+    for (int e = t; e < P * P; e += kBlock) mw[e] = w1[e];
+    for (int e = t; e < P; e += kBlock) mw[P * P + e] = b1[e];
+    for (int e = t; e < H * P; e += kBlock) mw[P * P + P + e] = w2[e];
+    for (int e = t; e < H; e += kBlock) mw[P * P + P + H * P + e] = b2[e];
+    __syncthreads();
+
+    // 1. pair bias, straight into the logit buffer (masked pairs: -inf in every head).  Rounds of
+    //    R pairs: their features (contiguous) staged with coalesced loads in the q/k/v region, which
+    //    is free until step 3; then a thread per pair runs the MLP with the hidden layer in registers.
+    {
+        const float* pb = pair + (int64_t)b * N * N * P;
+        const float* W1 = mw;
+        const float* B1 = mw + P * P;
+        const float* W2 = B1 + P;
+        const float* B2 = W2 + H * P;
+        float* fs = qs;                                      // [R][2P + 1]: features, then SiLU outputs
+        const int rl = 2 * P + 1;
+        const int cap = (L.lg - L.qs) / rl;                  // >= 1 by the layout
+        const int R = cap < kBlock ? cap : kBlock;
+        for (int p0 = 0; p0 < N * N; p0 += R) {
+            const int cnt = (N * N - p0) < R ? (N * N - p0) : R;
+            for (int e = t; e < cnt * P; e += kBlock) fs[(e / P) * rl + e % P] = pb[(int64_t)p0 * P + e];
+            __syncthreads();
+            const int pj = p0 + t;
+            if (t < cnt) {
+                if (mk[pj] < 0.5f) {
+                    for (int h = 0; h < H; ++h) lg[h * N * N + pj] = -INFINITY;
+                } else {
+                    float* row = fs + t * rl;
+                    for (int p = 0; p < P; ++p) {
+                        const float* w1r = W1 + p * P;
+                        float hs = B1[p];
+#pragma unroll 8
+                        for (int c = 0; c < P; ++c) hs = fmaf(w1r[c], row[c], hs);
+                        row[P + p] = hs / (1.f + exp_fast(-hs));
+                    }
+                    for (int h = 0; h < H; ++h) {
+                        const float* w2r = W2 + h * P;
+                        float bs = B2[h];
+#pragma unroll 8
+                        for (int p = 0; p < P; ++p) bs = fmaf(w2r[p], row[P + p], bs);
+                        lg[h * N * N + pj] = bs;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 2. LayerNorm in place: a wave per row
     for (int i = w; i < N; i += kWavesPerBlock) {
         float s = 0.f;
-        for (int d = lane; d < D; d += kWave) s += x[i * D + d];
+        for (int d = lane; d < D; d += kWave) s += xn[i * D + d];
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) s += shfl_xor(s, o);
         const float mean = s / D;
         float v2 = 0.f;
         for (int d = lane; d < D; d += kWave) {
-            const float c = x[i * D + d] - mean;
+            const float c = xn[i * D + d] - mean;
             v2 = fmaf(c, c, v2);
         }
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) v2 += shfl_xor(v2, o);
         const float rstd = 1.f / sqrtf(v2 / D + eps);
-        for (int d = lane; d < D; d += kWave) xn[i * D + d] = (x[i * D + d] - mean) * rstd * gamma[d] + beta[d];
+        for (int d = lane; d < D; d += kWave) xn[i * D + d] = (xn[i * D + d] - mean) * rstd * gamma[d] + beta[d];
     }
     __syncthreads();
 
-    // 2. q, k, v
-    rb_project(xn, N, D, wq, D, qs, D);
-    rb_project(xn, N, D, wk, D, ks, D);
-    rb_project(xn, N, D, wv, D, vs, D);
+    // 3. q, k, v
+    rb_project(xn, N, D, wq, D, qs, ld, wbuf);
+    rb_project(xn, N, D, wk, D, ks, ld, wbuf);
+    rb_project(xn, N, D, wv, D, vs, ld, wbuf);
 
-    // 3. pair bias, straight into the logit buffer (masked pairs: -inf in every head)
-    const float* pb = pair + (int64_t)b * N * N * P;
-    const float* mb = mask + (int64_t)b * N * N;
-    for (int pj = t; pj < N * N; pj += kBlock) {
-        if (mb[pj] < 0.5f) {
-            for (int h = 0; h < H; ++h) lg[h * N * N + pj] = -INFINITY;
-            continue;
-        }
-        const float* f = pb + (int64_t)pj * P;
-        float bias[kRbMaxHeads];
-#pragma unroll
-        for (int h = 0; h < kRbMaxHeads; ++h) bias[h] = h < H ? b2[h] : 0.f;
-        for (int p = 0; p < P; ++p) {
-            float hsum = b1[p];
-            for (int c = 0; c < P; ++c) hsum = fmaf(w1[p * P + c], f[c], hsum);
-            const float hid = hsum / (1.f + exp_fast(-hsum));
-#pragma unroll
-            for (int h = 0; h < kRbMaxHeads; ++h)
-                if (h < H) bias[h] = fmaf(w2[h * P + p], hid, bias[h]);
-        }
-#pragma unroll
-        for (int h = 0; h < kRbMaxHeads; ++h)
-            if (h < H) lg[h * N * N + pj] = bias[h];
-    }
-    __syncthreads();
-
-    // 4. logits
+    // 4. logits (lanes run along j: k rows padded to ld = D + 1 land in different banks)
     const float scale = 1.f / sqrtf((float)hd);
     for (int e = t; e < H * N * N; e += kBlock) {
         if (lg[e] == -INFINITY) continue;
         const int h = e / (N * N), i = (e / N) % N, j = e % N;
-        const float* qi = qs + i * D + h * hd;
-        const float* kj = ks + j * D + h * hd;
+        const float* qi = qs + i * ld + h * hd;
+        const float* kj = ks + j * ld + h * hd;
         float d = 0.f;
+#pragma unroll 8
         for (int c = 0; c < hd; ++c) d = fmaf(qi[c], kj[c], d);
         lg[e] = fmaf(d, scale, lg[e]);
     }
@@ -161,28 +243,28 @@ __global__ __launch_bounds__(kBlock) void relation_block_kernel(
         const int i = e / D, c = e % D, h = c / hd;
         const float* a = lg + (h * N + i) * N;
         float s = 0.f;
-        for (int j = 0; j < N; ++j) s = fmaf(a[j], vs[j * D + c], s);
+#pragma unroll 8
+        for (int j = 0; j < N; ++j) s = fmaf(a[j], vs[j * ld + c], s);
         o[e] = s;
     }
     __syncthreads();
 
     // 7. out = x + o Wo^T  (projected into q's buffer, then the residual at the store)
-    rb_project(o, N, D, wo, D, qs, D);
-    __syncthreads();
+    rb_project(o, N, D, wo, D, qs, ld, wbuf);
     float* ob = out + (int64_t)b * ND;
-    for (int e = t; e < ND; e += kBlock) ob[e] = x[e] + qs[e];
+    for (int e = t; e < ND; e += kBlock) ob[e] = x[e] + qs[(e / D) * ld + e % D];
 }
 
 }  // namespace
 
-size_t relation_block_lds_bytes(int N, int D, int H) { return ((size_t)4 * N * D + (size_t)H * N * N) * 4; }
+size_t relation_block_lds_bytes(int N, int D, int H, int P) { return (size_t)rb_layout(N, D, H, P).total * 4; }
 
 hipError_t launch_relation_block(const float* nodes, const float* pair, const float* mask, const float* gamma,
                                  const float* beta, float eps, const float* wq, const float* wk, const float* wv,
                                  const float* wo, const float* w1, const float* b1, const float* w2, const float* b2,
                                  int64_t B, int N, int D, int H, int P, float* out, hipStream_t stream) {
     if (B == 0 || N == 0) return hipSuccess;
-    const size_t lds = relation_block_lds_bytes(N, D, H);
+    const size_t lds = relation_block_lds_bytes(N, D, H, P);
     static bool attr_set = false;
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(relation_block_kernel),

@@ -250,4 +250,8 @@ def test_relation_block_host_checks(L):
     assert f(*args(4, 24, 96, 4, 16, nodes=None)) == NULL
     assert f(*args(4, 24, 96, 4, 16, out=ctypes.c_void_p(0x1004))) == ARGS
     assert f(*args(0, 24, 96, 4, 16, nodes=None, out=None)) == OK
-    assert L.gat_relation_block_lds_bytes(24, 96, 4, 16) == (4 * 24 * 96 + 4 * 24 * 24) * 4
+    up = lambda v: (v + 3) // 4 * 4  # noqa: E731
+    assert L.gat_relation_block_lds_bytes(24, 96, 4, 16) == 4 * (up(24 * 96) + 3 * up(24 * 97) + up(4 * 576) + up(576)
+                                                                 + up(16 * 16 + 16 + 64 + 4) + 2 * 16 * 100)
+    assert L.gat_relation_block_lds_bytes(4, 260, 4, 16) == 0
+    assert L.gat_relation_block_lds_bytes(24, 96, 4, 65) == 0
