@@ -69,10 +69,11 @@ class Oracle:
         L.oracle_softmax_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
         L.oracle_layer_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp]
         L.oracle_relation_attention.argtypes = [i64, i64, i32, i32, i32] + [vp] * 5 + [dbl] + [vp] * 8 + [vp]
+        L.oracle_linear.argtypes = [i64, i32, i32, vp, i32, vp, i32, vp, vp]
         for f in (L.oracle_sddmm, L.oracle_edge_softmax, L.oracle_aggregate,
                   L.oracle_softmax_aggregate, L.oracle_layer, L.oracle_edge_softmax_backward,
                   L.oracle_aggregate_backward, L.oracle_softmax_aggregate_backward, L.oracle_layer_backward,
-                  L.oracle_relation_attention):
+                  L.oracle_relation_attention, L.oracle_linear):
             f.restype = i32
 
     def num_threads(self) -> int:
@@ -229,6 +230,22 @@ class Oracle:
                                                 _p(w["beta"]), float(eps), _p(w["wq"]), _p(w["wk"]), _p(w["wv"]),
                                                 _p(w["wo"]), _p(w["w1"]), _p(w["b1"]), _p(w["w2"]), _p(w["b2"]),
                                                 _p(out))
+        assert rc == 0
+        return out
+
+    # --- node projections ---------------------------------------------------------------
+    def linear(self, x, w, bias=None) -> np.ndarray:
+        """out [M,N] = x [M,K] . w [N,K]^T + bias [N]; x and w fp32, bf16 bits (uint16) or fp64."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w)
+        assert x.ndim == 2 and w.ndim == 2 and x.shape[1] == w.shape[1]
+        M, K = x.shape
+        N = w.shape[0]
+        b = None if bias is None else np.ascontiguousarray(bias, np.float64)
+        assert b is None or b.shape == (N,)
+        out = np.full((M, N), np.nan, np.float64)
+        rc = self.lib.oracle_linear(M, K, N, _p(x), _dtype_code(x), _p(w), _dtype_code(w),
+                                    None if b is None else _p(b), _p(out))
         assert rc == 0
         return out
 

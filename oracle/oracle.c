@@ -20,6 +20,10 @@
  *   [l2_p37] CSR neighbourhood attention: softmax of the row's edge scores,
  *            then the weighted sum of node_value[col_idx[e]]; rows with no edges
  *            keep their zero output.
+ *   [l2_p4]  dense masked attention with a relation-MLP bias: LayerNorm, q/k/v
+ *            nn.Linear projections, biased masked softmax, output projection and
+ *            residual; its linear projections are also the node projections on
+ *            either side of the graph layer.
  * The full layer (scores from q_i . k_j, then softmax, then aggregation of v)
  * is the composition of the three steps above; no single page writes it out.
  * The backward functions at the end are the derivatives of these definitions
@@ -454,6 +458,28 @@ int oracle_relation_attention(int64_t B, int64_t N, int D, int H, int P, const d
             }
         }
         free(xn); free(q); free(k); free(v); free(o); free(lg); free(hid);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Node projection: the nn.Linear steps on either side of the attention in the l2_p4 reference
+ * model (the q/k/v projections of the node rows and the output projection):
+ *   out[m, n] = bias[n] + sum_k x[m, k] * w[n, k]      (w stored [out_features, in_features])
+ * x [M,K] and w [N,K] as fp32, bf16 (raw bits) or fp64, widened exactly; bias [N] double, or
+ * NULL for none; out [M,N] double.
+ * ------------------------------------------------------------------------------------------ */
+int oracle_linear(int64_t M, int K, int N, const void* x, int x_dtype, const void* w, int w_dtype,
+                  const double* bias, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int n = 0; n < N; ++n) {
+            double s = bias ? bias[n] : 0.0;
+            for (int k = 0; k < K; ++k)
+                s += load_feat(x, x_dtype, m * K + k) * load_feat(w, w_dtype, (int64_t)n * K + k);
+            out[m * N + n] = s;
+        }
     }
     return 0;
 }

@@ -453,12 +453,68 @@ def pin_relation_attention_closed_forms(orc):
     np.testing.assert_allclose(permuted, out[:, perm], rtol=1e-12, atol=1e-12)
 
 
+def pin_linear_torch(orc):
+    """Against torch's nn.functional.linear in fp64 (weights stored [out, in]), with and without
+    bias, on fp64, fp32 and bf16-bit inputs (the bf16 values decoded by numpy)."""
+    import torch
+    import torch.nn.functional as F
+    r = _rng(51)
+    for M, K, N in [(7, 13, 5), (1, 64, 96), (33, 8, 1), (16, 256, 40)]:
+        x = r.standard_normal((M, K))
+        w = r.standard_normal((N, K))
+        b = r.standard_normal(N)
+        ref = F.linear(torch.tensor(x), torch.tensor(w), torch.tensor(b)).numpy()
+        np.testing.assert_allclose(orc.linear(x, w, b), ref, rtol=1e-12, atol=1e-12)
+        ref0 = F.linear(torch.tensor(x), torch.tensor(w)).numpy()
+        np.testing.assert_allclose(orc.linear(x, w), ref0, rtol=1e-12, atol=1e-12)
+        xb = G.f32_to_bf16_bits(x.astype(np.float32))
+        wf = w.astype(np.float32)
+        refb = F.linear(torch.tensor(G.bf16_bits_to_f32(xb).astype(np.float64)),
+                        torch.tensor(wf.astype(np.float64)), torch.tensor(b)).numpy()
+        np.testing.assert_allclose(orc.linear(xb, wf, b), refb, rtol=1e-12, atol=1e-12)
+
+
+def pin_linear_integer_exact(orc):
+    """Small integers: every product and sum is exact in double, so the result equals numpy's
+    int64 x @ w.T + b exactly."""
+    r = _rng(52)
+    x = r.integers(-9, 10, (11, 19))
+    w = r.integers(-9, 10, (6, 19))
+    b = r.integers(-50, 51, 6)
+    got = orc.linear(x.astype(np.float64), w.astype(np.float32), b.astype(np.float64))
+    assert np.array_equal(got, (x @ w.T + b).astype(np.float64))
+
+
+def pin_linear_closed_forms(orc):
+    """Identity weights return x + b; a one-hot input row returns that column of w plus b; zero
+    input returns the bias on every row; reordering w's rows reorders the output columns;
+    reordering the K axis of both operands changes nothing; no rows gives an empty result."""
+    r = _rng(53)
+    M, K, N = 9, 12, 7
+    x = r.standard_normal((M, K))
+    b = r.standard_normal(K)
+    assert np.array_equal(orc.linear(x, np.eye(K), b), x + b)
+    w = r.standard_normal((N, K))
+    bn = r.standard_normal(N)
+    onehot = np.zeros((K, K))
+    onehot[np.arange(K), np.arange(K)] = 1.0
+    np.testing.assert_allclose(orc.linear(onehot, w, bn), w.T + bn, rtol=1e-15, atol=0)
+    assert np.array_equal(orc.linear(np.zeros((M, K)), w, bn), np.broadcast_to(bn, (M, N)))
+    out = orc.linear(x, w, bn)
+    perm = r.permutation(N)
+    np.testing.assert_allclose(orc.linear(x, w[perm], bn[perm]), out[:, perm], rtol=1e-13, atol=1e-13)
+    kp = r.permutation(K)
+    np.testing.assert_allclose(orc.linear(x[:, kp], w[:, kp], bn), out, rtol=1e-12, atol=1e-12)
+    assert orc.linear(np.zeros((0, K)), w, bn).shape == (0, N)
+
+
 ALL_PINS = [pin_sddmm_dense, pin_sddmm_integer_exact, pin_softmax_closed_forms, pin_softmax_dense,
             pin_softmax_invariants, pin_aggregate_dense, pin_aggregate_integer_exact,
             pin_zero_rows_positive_zero, pin_softmax_aggregate_dense, pin_softmax_aggregate_closed_forms,
             pin_layer_dense, pin_backward_finite_differences, pin_layer_backward_autograd,
             pin_backward_invariants, pin_aggregate_backward_integer_exact, pin_relation_attention_torch,
-            pin_relation_attention_closed_forms]
+            pin_relation_attention_closed_forms, pin_linear_torch, pin_linear_integer_exact,
+            pin_linear_closed_forms]
 
 
 def run_all(orc) -> list:

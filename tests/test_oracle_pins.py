@@ -77,6 +77,12 @@ MUTANTS = [
      "if (mask[(b * N + i) * N + j] > 0.5) continue;"),
     ("relblock_residual_dropped", "out[(b * N + i) * D + r] = x[i * D + r] + s;", "out[(b * N + i) * D + r] = s;"),
     ("relblock_bias_head0", "rb += w2[h * P + p] * hid[p];", "rb += w2[p] * hid[p];"),
+    # node projections
+    ("linear_weight_transposed", "load_feat(w, w_dtype, (int64_t)n * K + k);", "load_feat(w, w_dtype, (int64_t)k * N + n);"),
+    ("linear_bias_dropped", "double s = bias ? bias[n] : 0.0;", "double s = 0.0;"),
+    ("linear_k_off_by_one", "for (int k = 0; k < K; ++k)\n                s += load_feat(x",
+     "for (int k = 1; k < K; ++k)\n                s += load_feat(x"),
+    ("linear_x_row_wrong", "s += load_feat(x, x_dtype, m * K + k)", "s += load_feat(x, x_dtype, k)"),
 ]
 
 
