@@ -224,6 +224,32 @@ gat_status gat_relation_block(const float* nodes, const float* pair_feats, const
                               int n_nodes, int dim, int heads, int pair_dim, float* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Node projections: the nn.Linear steps of the l2_p4 page's reference model (its q/k/v
+ * projections of the node rows and its output projection), which sit on either side of the
+ * graph layer above.
+ *   y[m, n] = bias[n] + sum_k x[m, k] * w[n, k]     for 0 <= m < n_rows, 0 <= n < n_cols
+ *   x     [n_rows, in_dim] of x_dtype, row-major.  GAT_F32 values are rounded to bfloat16
+ *         (nearest, ties to even) before they are multiplied; GAT_BF16 values are used as is.
+ *   w     bfloat16 bits [n_cols, in_dim], row-major (nn.Linear's [out_features, in_features])
+ *   bias  fp32 [n_cols], or NULL for none
+ *   out   HOST array of n_out device pointers (1 <= n_out <= 3); out[s] is
+ *         [n_rows, n_cols / n_out] of y_dtype, row-major, and receives y's columns
+ *         [s * n_cols / n_out, (s + 1) * n_cols / n_out).  With w = [Wq; Wk; Wv] and n_out = 3,
+ *         one call writes q, k and v in the [rows, heads, head_dim] layout the layer reads,
+ *         reading x once.
+ * Arithmetic: bf16 x bf16 products are exact in fp32; sums are fp32, in an order fixed by the
+ * tiling (independent of the launch).  y is stored as fp32, or rounded to bf16 (nearest, ties
+ * to even).  in_dim = 0 gives y = bias (or zeros).
+ * Requirements: in_dim in [0, 65536] and a multiple of 8, n_cols in [1, 65536] and a multiple
+ * of n_out (GAT_ERR_UNSUPPORTED otherwise); n_rows in [0, 2^31 - 1] with at most 2^24 tiles of
+ * 128 x 128 (GAT_ERR_SIZE); x and w 16-byte aligned (GAT_ERR_ARGS).  The output arrays must
+ * not overlap each other, x, w or bias.
+ * ------------------------------------------------------------------------------------------ */
+gat_status gat_linear(const void* x, gat_dtype x_dtype, const uint16_t* w, const float* bias, int64_t n_rows,
+                      int in_dim, int n_cols, void* const* out, int n_out, gat_dtype y_dtype,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Backward.  No page writes the backward pass out; the l1_p10 page (edge-only SDDMM, the
  * passage on the backward pass) notes that gradients sum into the feature rows that edges read.
  * Each entry point below computes the derivative of a forward entry point above, given

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "kernels.hpp"
+#include "linear.hpp"
 
 namespace gat {
 hipError_t launch_spmm_agg(int, int, int, const int32_t*, const int32_t*, int64_t, int64_t, const float*,
@@ -376,6 +377,33 @@ gat_status gat_relation_block(const float* nodes, const float* pair_feats, const
         if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return GAT_ERR_ARGS;   // 16-byte row loads
     return hip_status(gat::launch_relation_block(nodes, pair_feats, edge_mask, gamma, beta, eps, wq, wk, wv, wo, w1,
                                                  b1, w2, b2, batch, n_nodes, dim, heads, pair_dim, out, stream));
+}
+
+// ------------------------------------------------------------------------------ projections
+gat_status gat_linear(const void* x, gat_dtype x_dtype, const uint16_t* w, const float* bias, int64_t n_rows,
+                      int in_dim, int n_cols, void* const* out, int n_out, gat_dtype y_dtype,
+                      hipStream_t stream) {
+    if (!size_ok(n_rows)) return GAT_ERR_SIZE;
+    if ((x_dtype != GAT_F32 && x_dtype != GAT_BF16) || (y_dtype != GAT_F32 && y_dtype != GAT_BF16) ||
+        in_dim < 0 || in_dim > 65536 || in_dim % 8 != 0 || n_out < 1 || n_out > gat::kLinMaxOut || n_cols < 1 ||
+        n_cols > 65536 || n_cols % n_out != 0)
+        return GAT_ERR_UNSUPPORTED;
+    const int64_t tiles = (n_rows + 127) / 128 * ((n_cols + 127) / 128);
+    if (tiles > (int64_t{1} << 24)) return GAT_ERR_SIZE;       // grid of 256-thread workgroups
+    if (out == nullptr) return GAT_ERR_NULL;
+    if (n_rows == 0) return GAT_OK;                              // empty output arrays may be NULL
+    gat::LinearOut o{};
+    o.width = n_cols / n_out;
+    for (int s = 0; s < n_out; ++s) {
+        if (out[s] == nullptr) return GAT_ERR_NULL;
+        o.p[s] = out[s];
+    }
+    if (in_dim > 0) {
+        if (x == nullptr || w == nullptr) return GAT_ERR_NULL;
+        if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(w) % 16 != 0) return GAT_ERR_ARGS;
+    }
+    return hip_status(gat::launch_linear(x, x_dtype == GAT_BF16, w, bias, n_rows, in_dim, n_cols, o,
+                                         y_dtype == GAT_BF16, stream));
 }
 
 // ------------------------------------------------------------------------------ backward

@@ -9,6 +9,7 @@ library or a CPU tensor raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -26,7 +27,7 @@ EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge
             "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof",
             "gat_csc_workspace_bytes", "gat_csc_sizeof", "gat_csc_build", "gat_edge_softmax_backward",
             "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward",
-            "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block"]
+            "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block", "gat_linear"]
 
 
 class GatError(RuntimeError):
@@ -91,9 +92,10 @@ def _lib():
     L.gat_relation_block_lds_bytes.argtypes = [i32, i32, i32, i32]
     L.gat_relation_block_lds_bytes.restype = sz
     L.gat_relation_block.argtypes = [vp, vp, vp, vp, vp, f32] + [vp] * 8 + [i64, i32, i32, i32, i32, vp, vp]
+    L.gat_linear.argtypes = [vp, i32, vp, vp, i64, i32, i32, ctypes.POINTER(vp), i32, i32, vp]
     for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer,
               L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward,
-              L.gat_batch_csr, L.gat_relation_block):
+              L.gat_batch_csr, L.gat_relation_block, L.gat_linear):
         f.restype = i32
     L.gat_status_str.argtypes = [i32]
     L.gat_status_str.restype = ctypes.c_char_p
@@ -430,4 +432,36 @@ def gat_relation_block(nodes, pair_feats, edge_mask, params: dict, eps: float = 
     _check("gat_relation_block", _lib().gat_relation_block(
         _ptr(nodes), _ptr(pair_feats), _ptr(edge_mask), *(_ptr(params[n]) for n in names[:2]), float(eps),
         *(_ptr(params[n]) for n in names[2:]), B, N, D, H, P, _ptr(out), _stream(stream)))
+    return out
+
+
+def gat_linear(x, w, bias=None, n_out: int = 1, y_dtype=torch.float32, out=None, stream=None):
+    """y = x . w^T + bias on the matrix cores (bf16 operands, fp32 sums).  x [M, ...] fp32 or bf16 with its
+    trailing dims flattened to K; w bf16 [N, K]; bias fp32 [N] or None.  Returns a list of n_out tensors
+    [M, N / n_out] of y_dtype (fp32 or bf16) holding y's column blocks in order; `out` may supply them."""
+    _dev(x, "x")
+    _dev(w, "w", torch.bfloat16, 2)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, 1)
+    M = x.shape[0]
+    K = math.prod(x.shape[1:])
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w is {tuple(w.shape)} but x rows have {K} elements")
+    if y_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("y_dtype must be float32 or bfloat16")
+    if n_out < 1 or N % n_out != 0:
+        raise ValueError(f"{N} output columns do not split into {n_out} arrays")
+    if out is None:
+        out = [torch.empty((M, N // n_out), dtype=y_dtype, device=w.device) for _ in range(n_out)]
+    if len(out) != n_out:
+        raise ValueError(f"expected {n_out} output arrays")
+    for o in out:
+        _dev(o, "out", y_dtype)
+        if o.numel() != M * (N // n_out):
+            raise ValueError("output array of the wrong size")
+    ptrs = (ctypes.c_void_p * n_out)(*(o.data_ptr() for o in out))
+    _check("gat_linear", _lib().gat_linear(
+        _ptr(x), _feat_dtype(x), _ptr(w), _ptr(bias), M, K, N, ptrs, n_out,
+        GAT_BF16 if y_dtype == torch.bfloat16 else GAT_F32, _stream(stream)))
     return out

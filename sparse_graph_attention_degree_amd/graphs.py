@@ -366,6 +366,26 @@ def make_relation_block(B: int, N: int, D: int, H: int, P: int, seed: int = 0, m
     return nodes, pair, m, params
 
 
+# Node projections around the c4 layer: 2^20 node rows of model dimension H*D = 256 in, the
+# q/k/v projection to 3 * 256 columns (bf16 out, the layer's input dtype) and the output
+# projection from the layer's fp32 output back to 256 columns.
+PROJECTION = dict(M=2**20, K=256, heads=4, head_dim=64)
+
+
+def make_linear(M: int, K: int, N: int, seed: int = 0, x_dtype: str = "bf16", bias: bool = True):
+    """(x [M,K], w [N,K] bf16 bits, bias [N] fp32 or None).  x: N(0,1) as fp32, or bf16 bits
+    (rounded to nearest even); w: nn.Linear's U(-1/sqrt(K), 1/sqrt(K)) rounded to bf16."""
+    r = np.random.default_rng(np.random.SeedSequence([seed, 0x11AE]))
+    x = r.standard_normal((M, K), dtype=np.float32)
+    if x_dtype == "bf16":
+        x = f32_to_bf16_bits(x)
+    elif x_dtype != "f32":
+        raise ValueError(x_dtype)
+    bound = 1.0 / np.sqrt(max(K, 1))
+    w = f32_to_bf16_bits(r.uniform(-bound, bound, (N, K)).astype(np.float32))
+    b = r.uniform(-bound, bound, N).astype(np.float32) if bias else None
+    return x, w, b
+
 def batch_arrays(graphs):
     """The inputs of a block-diagonal batch: the graphs' row_ptr and col_idx concatenated as they
     are, and int32 prefix sums [B+1] of their rows, edges and sources."""

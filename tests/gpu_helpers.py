@@ -47,6 +47,21 @@ def assert_close(got, want, kind: str, what: str = ""):
     return float(err.max()) if err.size else 0.0
 
 
+def assert_close_sum(got, want, mag, kind: str, what: str = ""):
+    """Gradients are sums of many signed terms (a source read by thousands of edges, a softmax
+    row): |got - want| <= atol + rtol * (|want| + mag), where mag is the same sum taken over the
+    terms' absolute values (rtol is then the relative error of a sum, as fp32 accumulation gives)."""
+    atol, rtol = TOL[kind]
+    got, want, mag = (np.asarray(a, dtype=np.float64) for a in (got, want, mag))
+    assert got.shape == want.shape == mag.shape and np.all(np.isfinite(got)), what
+    err = np.abs(got - want)
+    bad = err > atol + rtol * (np.abs(want) + mag)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err, 0)), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} out of tolerance; worst at {i}: got {got[i]!r} "
+                             f"want {want[i]!r} (term magnitude {mag[i]!r})")
+
+
 def assert_positive_zero_rows(out: np.ndarray, deg: np.ndarray, what=""):
     z = deg == 0
     assert np.all(out[z] == 0.0) and not np.any(np.signbit(out[z])), f"{what}: zero rows not +0.0"

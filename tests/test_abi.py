@@ -255,3 +255,28 @@ def test_relation_block_host_checks(L):
                                                                  + up(16 * 16 + 16 + 64 + 4) + 2 * 16 * 100)
     assert L.gat_relation_block_lds_bytes(4, 260, 4, 16) == 0
     assert L.gat_relation_block_lds_bytes(24, 96, 4, 65) == 0
+
+
+def test_linear_host_checks(L):
+    f = L.gat_linear
+    outs = (ctypes.c_void_p * 3)(0x1000, 0x2000, 0x3000)
+
+    def call(M=10, K=64, N=96, n_out=1, x=FAKE, w=FAKE, out=outs, xd=0, yd=0):
+        return f(x, xd, w, None, M, K, N, out, n_out, yd, None)
+
+    assert call(M=-1) == SIZE
+    assert call(M=2**31) == SIZE
+    assert call(M=2**31 - 1, N=65536) == SIZE          # more than 2^24 tiles
+    assert call(K=12) == UNSUP
+    assert call(K=-8) == UNSUP
+    assert call(K=65544) == UNSUP
+    assert call(N=0) == UNSUP
+    assert call(N=97, n_out=3) == UNSUP
+    assert call(n_out=0) == UNSUP and call(n_out=4) == UNSUP
+    assert call(xd=2) == UNSUP and call(yd=7) == UNSUP
+    assert call(out=None) == NULL
+    assert call(N=96, n_out=3, out=(ctypes.c_void_p * 3)(0x1000, None, 0x3000)) == NULL
+    assert call(x=None) == NULL and call(w=None) == NULL
+    assert call(x=ctypes.c_void_p(0x1002)) == ARGS
+    assert call(w=ctypes.c_void_p(0x1008)) == ARGS
+    assert call(M=0) == OK                              # nothing to do: returns before any launch

@@ -8,24 +8,10 @@ import pytest
 import oracle
 from sparse_graph_attention_degree_amd import gat
 from sparse_graph_attention_degree_amd import graphs as G
-from tests.gpu_helpers import TOL, assert_close, assert_positive_zero_rows, mixed_graph, to_dev, to_np
+from tests.gpu_helpers import (assert_close, assert_close_sum, assert_positive_zero_rows, mixed_graph, to_dev,
+                               to_np)
 
 pytestmark = pytest.mark.gpu
-
-
-def assert_close_sum(got, want, mag, kind: str, what: str = ""):
-    """Gradients are sums of many signed terms (a source read by thousands of edges, a softmax
-    row): |got - want| <= atol + rtol * (|want| + mag), where mag is the same sum taken over the
-    terms' absolute values (rtol is then the relative error of a sum, as fp32 accumulation gives)."""
-    atol, rtol = TOL[kind]
-    got, want, mag = (np.asarray(a, dtype=np.float64) for a in (got, want, mag))
-    assert got.shape == want.shape == mag.shape and np.all(np.isfinite(got)), what
-    err = np.abs(got - want)
-    bad = err > atol + rtol * (np.abs(want) + mag)
-    if bad.any():
-        i = np.unravel_index(np.argmax(np.where(bad, err, 0)), err.shape)
-        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} out of tolerance; worst at {i}: got {got[i]!r} "
-                             f"want {want[i]!r} (term magnitude {mag[i]!r})")
 
 
 def _f64(a):
