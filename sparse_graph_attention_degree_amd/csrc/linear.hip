@@ -31,11 +31,16 @@ constexpr int kPitch = kBK + 8;               // bf16 elements per LDS row
 constexpr int kLinThreads = 256;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ uint32_t to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;     // NaN stays a (quiet) NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 lin_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float lin_f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 bits (lo in the low half) with gfx950's v_cvt_pk_bf16_f32: round to
+// nearest, ties to even; a NaN stays a NaN.
+__device__ __forceinline__ uint32_t bf16_pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((lin_f32x2){lo, hi}, lin_bf16x2));
 }
+
+__device__ __forceinline__ uint32_t to_bf16_rne(float f) { return bf16_pack2(f, 0.0f) & 0xffffu; }
 
 // Workgroup b runs on XCD b % 8.  Give XCD x a contiguous range of tiles so that the column
 // tiles of one row block run on one XCD, close in time.
@@ -80,9 +85,8 @@ struct PanelF32 {
         const int c = (t & 15) * 4;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            uint2 h;
-            h.x = to_bf16_rne(__uint_as_float(v[i].x)) | (to_bf16_rne(__uint_as_float(v[i].y)) << 16);
-            h.y = to_bf16_rne(__uint_as_float(v[i].z)) | (to_bf16_rne(__uint_as_float(v[i].w)) << 16);
+            const uint2 h = make_uint2(bf16_pack2(__uint_as_float(v[i].x), __uint_as_float(v[i].y)),
+                                       bf16_pack2(__uint_as_float(v[i].z), __uint_as_float(v[i].w)));
             *reinterpret_cast<uint2*>(lds + ((t >> 4) + 16 * i) * kPitch + c) = h;
         }
     }
@@ -175,6 +179,334 @@ __global__ __launch_bounds__(kLinThreads, 2) void linear_kernel(const XT* __rest
     }
 }
 
+// ------------------------------------------------------------------ stationary weights, K <= 256
+// For in_dim <= 256 a wave keeps its w fragments for the whole of K in registers (2 column
+// tiles x 16 k-steps = 128 VGPRs), so w is read once per workgroup and only x streams.  A
+// 256-thread workgroup owns 256 output columns (one column group of 64 per wave, each wave
+// covering all rows of a block as 32-row MFMA tiles) and walks a strided stream of row blocks
+// of x (64 rows of bf16 x, 32 of fp32 x): blocks i + 1 and i + 2 wait in registers while block
+// i, in LDS, feeds the MFMAs (each 16-byte fragment of x read from LDS feeds two MFMAs); then
+// block i + 1 goes to the other LDS buffer and block i + 3 is fetched into its registers.
+// Vector-memory waits count in issue order, so each fetch precedes the block's stores and the
+// number of loads and stores per block is fixed (buffer accesses, no branches): waiting for a
+// fetched block then leaves every later access in flight.  The results leave through a row-major
+// LDS stage as whole 16-byte pieces of rows.  The grid holds one
+// workgroup per CU; the column blocks of one row stream are consecutive after the XCD remap, so
+// the q, k and v workgroups of the same rows share one XCD's L2 copy of x.
+constexpr int kWsK = 256;                  // largest in_dim of this path
+constexpr int kWsKK = kWsK / 16;           // MFMA k-steps
+// rows per block: 64 for bf16 x, 32 for fp32 x (whose staging registers are twice as many)
+template <bool XF32>
+constexpr int ws_rows() { return XF32 ? 32 : 64; }
+constexpr int kWsCols = 256;               // columns per workgroup
+constexpr int kWsThreads = 256;            // 4 column groups of 64
+constexpr int kWsPitch = kWsK + 8;         // bf16 per LDS row (528 bytes: rows 4 banks apart)
+
+typedef unsigned int lin_u32x4 __attribute__((ext_vector_type(4)));
+
+// Blocks of x and y are addressed through buffer descriptors (base, size in bytes) rebuilt per
+// block: a byte offset at or past the size reads 0 and drops a write, so edge rows and columns
+// need no branches.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lin_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 lin_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    const lin_u32x4 v = __builtin_bit_cast(lin_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool XF32>
+struct RowBlock;
+
+// 64 rows x 256 bf16 = 2048 pieces of 16 bytes, eight per thread (32 threads per row)
+template <>
+struct RowBlock<false> {
+    uint4 v[8];
+    __device__ __forceinline__ void fetch(const void* xv, int64_t M, int K, int64_t r0, int t) {
+        const int64_t rows = r0 >= M ? 0 : M - r0 < 64 ? M - r0 : 64;
+        const auto rs = lin_rsrc(static_cast<const uint16_t*>(xv) + (rows > 0 ? r0 * K : 0),
+                                 static_cast<uint32_t>(rows * K * 2));
+        const int c = (t & 31) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off = c < K ? static_cast<uint32_t>((((t >> 5) + 8 * i) * K + c) * 2) : kOob;
+            v[i] = lin_load16(rs, off);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
+        const int c = (t & 31) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + ((t >> 5) + 8 * i) * kWsPitch + c) = v[i];
+    }
+};
+
+// 32 rows x 256 fp32 = 2048 pieces, eight per thread (64 threads per row), rounded to bf16
+template <>
+struct RowBlock<true> {
+    uint4 v[8];
+    __device__ __forceinline__ void fetch(const void* xv, int64_t M, int K, int64_t r0, int t) {
+        const int64_t rows = r0 >= M ? 0 : M - r0 < 32 ? M - r0 : 32;
+        const auto rs = lin_rsrc(static_cast<const float*>(xv) + (rows > 0 ? r0 * K : 0),
+                                 static_cast<uint32_t>(rows * K * 4));
+        const int c = (t & 63) * 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off = c < K ? static_cast<uint32_t>((((t >> 6) + 4 * i) * K + c) * 4) : kOob;
+            v[i] = lin_load16(rs, off);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
+        const int c = (t & 63) * 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint2 h = make_uint2(bf16_pack2(__uint_as_float(v[i].x), __uint_as_float(v[i].y)),
+                                       bf16_pack2(__uint_as_float(v[i].z), __uint_as_float(v[i].w)));
+            *reinterpret_cast<uint2*>(lds + ((t >> 6) + 4 * i) * kWsPitch + c) = h;
+        }
+    }
+};
+
+template <bool XF32, bool Y_BF16, bool BUF>
+__global__ __launch_bounds__(kWsThreads, 1) void linear_wstat_kernel(const void* __restrict__ x,
+                                                                     const uint16_t* __restrict__ w,
+                                                                     const float* __restrict__ bias, int64_t M,
+                                                                     int K, int N, LinearOut out, int n_col_blocks,
+                                                                     int64_t n_streams, int64_t n_row_blocks,
+                                                                     int vec) {
+    static_assert(kWsThreads == kWsCols, "one bias entry per thread");
+    constexpr int kRows = ws_rows<XF32>();
+    constexpr int kTi = kRows / 32;                               // MFMA row tiles per block
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kRows * kWsPitch];
+    __shared__ __attribute__((aligned(16))) float bs[kWsCols];
+    constexpr int kYB = Y_BF16 ? 2 : 4;                          // bytes per output element
+    constexpr int kOsPitch = (kWsCols + 16 / kYB) * kYB;         // stage row bytes, padded by 16
+    __shared__ __attribute__((aligned(16))) char ostage[kRows * kOsPitch];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t g = xcd_tile(blockIdx.x, gridDim.x);
+    const int cb = static_cast<int>(g % n_col_blocks);
+    const int64_t first = g / n_col_blocks;
+    const int fr = lane & 31, fk = (lane >> 5) * 8;
+
+    // The MFMA's A operand is w (32 output columns x 16 k) and its B operand x^T (16 k x 32 rows),
+    // so the accumulator holds a tile of y^T: register 4 q + e of lane l is y[row l % 32]
+    // [column 8 q + 4 (l / 32) + e], four consecutive columns of one row per lane, stored as one
+    // vector.  This wave's two column tiles of w over the whole of K, zero past N and K:
+    // All 16 k-steps run for any K <= 256: w fragments and the x block in LDS are zero past K,
+    // so the steps past K add exact zeros.
+    constexpr int NKK = kWsKK;
+    lin_bf16x8 wf[2][NKK];
+    {
+        uint4 wv[2][NKK];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int wcol = cb * kWsCols + wave * 64 + 32 * j + fr;
+            const bool cin = wcol < N;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int k = kk * 16 + fk;
+                wv[j][kk] = (cin && k < K) ? ld16(w + static_cast<int64_t>(wcol) * K + k) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                lin_u32x4 u = {wv[j][kk].x, wv[j][kk].y, wv[j][kk].z, wv[j][kk].w};
+                asm volatile("" : "+a"(u));           // keep w in AGPRs (an MFMA operand may live there)
+                wf[j][kk] = __builtin_bit_cast(lin_bf16x8, u);
+            }
+    }
+    {
+        const int c = cb * kWsCols + t;
+        bs[t] = (bias != nullptr && c < N) ? bias[c] : 0.0f;
+    }
+
+    int64_t blk = first;
+    if (blk >= n_row_blocks) return;                  // uniform over the workgroup
+    // Blocks p + 1 and p + 2 of this stream wait in registers (rb0, rb1 in turn) while block p is
+    // computed from LDS: 64 KB of x in flight per CU.  A fetch past the last block reads nothing
+    // (empty descriptor), so every step issues the same loads and stores.
+    RowBlock<XF32> rb0, rb1;
+    rb0.fetch(x, M, K, blk * kRows, t);
+    rb0.store(xs[0], t);
+    rb0.fetch(x, M, K, (blk + n_streams) * kRows, t);
+    const auto none = lin_rsrc(out.p[0], 0);
+    constexpr int kStores = kRows * (kWsCols * kYB / 16) / kWsThreads;     // epilogue stores per step
+    // As many dropped stores (past an empty descriptor) as a step issues, so that every fetch is
+    // followed by the same memory instructions on every path and its wait leaves them in flight.
+    auto dummy_stores = [&]() {
+        if (BUF) {
+#pragma unroll
+            for (int u = 0; u < kStores; ++u)
+                __builtin_amdgcn_raw_buffer_store_b128((gat_v4i){0, 0, 0, 0}, none, kOob + 16 * u, 0, 0);
+        }
+    };
+    dummy_stores();
+    rb1.fetch(x, M, K, (blk + 2 * n_streams) * kRows, t);
+    dummy_stores();
+    __syncthreads();
+
+    const int cl0 = wave * 64 + 4 * (lane >> 5);     // block-local column of this lane's first quad
+    const int width = out.width;
+    float bq[2][16];                                  // bias of accumulator register r of tile j
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 b4 = *reinterpret_cast<const float4*>(&bs[cl0 + 32 * j + 8 * q]);
+            bq[j][4 * q] = b4.x;
+            bq[j][4 * q + 1] = b4.y;
+            bq[j][4 * q + 2] = b4.z;
+            bq[j][4 * q + 3] = b4.w;
+        }
+    // one block: compute from xcur, move the next block from rbc to xnext, refill rbc three
+    // blocks ahead, store the results; false after the stream's last block
+    auto step = [&](RowBlock<XF32>& rbc, const uint16_t* xcur, uint16_t* xnext) -> bool {
+        lin_f32x16 acc[kTi][2];                      // start from the bias: y = b + sum_k x w
+#pragma unroll
+        for (int i = 0; i < kTi; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = bq[j][r];
+        const uint16_t* arow = &xcur[fr * kWsPitch + fk];
+        lin_bf16x8 a[2][kTi];                        // fragments of step kk (kk & 1) and kk + 1
+#pragma unroll
+        for (int i = 0; i < kTi; ++i) a[0][i] = *reinterpret_cast<const lin_bf16x8*>(arow + 32 * i * kWsPitch);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int c = kk & 1;
+            if (kk + 1 < NKK) {
+#pragma unroll
+                for (int i = 0; i < kTi; ++i)
+                    a[c ^ 1][i] = *reinterpret_cast<const lin_bf16x8*>(arow + 32 * i * kWsPitch + (kk + 1) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < kTi; ++i) {
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][kk], a[c][i], acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][kk], a[c][i], acc[i][1], 0, 0, 0);
+            }
+        }
+        const int64_t nxt = blk + n_streams;
+        const bool more = nxt < n_row_blocks;
+        if (more) rbc.store(xnext, t);
+        rbc.fetch(x, M, K, (nxt + 2 * n_streams) * kRows, t);
+        // Epilogue through LDS: the accumulators (plus bias, rounded if bf16) go to a row-major
+        // stage, then every thread stores whole 16-byte pieces of consecutive columns, so one wave
+        // instruction writes 1 KB of complete rows.
+#pragma unroll
+        for (int i = 0; i < kTi; ++i) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int cl = cl0 + 32 * j + 8 * q;
+                    const float y0 = acc[i][j][4 * q], y1 = acc[i][j][4 * q + 1];
+                    const float y2 = acc[i][j][4 * q + 2], y3 = acc[i][j][4 * q + 3];
+                    char* dst = ostage + (32 * i + fr) * kOsPitch + cl * kYB;
+                    if (Y_BF16)
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_pack2(y0, y1), bf16_pack2(y2, y3));
+                    else
+                        *reinterpret_cast<float4*>(dst) = make_float4(y0, y1, y2, y3);
+                }
+            }
+        }
+        __syncthreads();
+        {
+            constexpr int kEpp = 16 / kYB;                       // columns per 16-byte piece
+            constexpr int kPiecesPerRow = kWsCols / kEpp;
+            constexpr int kRowsPerPass = kWsThreads / kPiecesPerRow;
+            const int cl = (t % kPiecesPerRow) * kEpp;
+            const int c = cb * kWsCols + cl;
+            if (BUF) {
+                // every column of this workgroup lies in one output array
+                const int cbase = cb * kWsCols;
+                const int seg = (cbase >= width) + (cbase >= 2 * width);
+                char* p = static_cast<char*>(seg == 0 ? out.p[0] : (seg == 1 ? out.p[1] : out.p[2]));
+                const int64_t r0 = blk * kRows;
+                const int64_t rows = M - r0 < kRows ? M - r0 : kRows;
+                const auto rs = lin_rsrc(p + r0 * width * kYB, static_cast<uint32_t>(rows * width * kYB));
+                const int cc = c - seg * width;
+#pragma unroll
+                for (int u = 0; u < kRows / kRowsPerPass; ++u) {
+                    const int rl = t / kPiecesPerRow + kRowsPerPass * u;
+                    const uint32_t off = c + kEpp <= N ? static_cast<uint32_t>((rl * width + cc) * kYB) : kOob;
+                    const uint4 v = *reinterpret_cast<const uint4*>(ostage + rl * kOsPitch + cl * kYB);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(gat_v4i, (lin_u32x4){v.x, v.y, v.z, v.w}),
+                                                           rs, off, 0, 0);
+                }
+            } else {
+#pragma unroll
+            for (int u = 0; u < kRows / kRowsPerPass; ++u) {
+                const int rl = t / kPiecesPerRow + kRowsPerPass * u;
+                const int64_t row = blk * kRows + rl;
+                if (row >= M || c >= N) continue;
+                const char* src = ostage + rl * kOsPitch + cl * kYB;
+                if (vec && c + kEpp <= N) {
+                    const int seg = (c >= width) + (c >= 2 * width);
+                    char* p = static_cast<char*>(seg == 0 ? out.p[0] : (seg == 1 ? out.p[1] : out.p[2]));
+                    *reinterpret_cast<uint4*>(p + (row * width + (c - seg * width)) * kYB) =
+                        *reinterpret_cast<const uint4*>(src);
+                } else {
+                    for (int e = 0; e < kEpp && c + e < N; ++e) {
+                        const int ce = c + e;
+                        const int seg = (ce >= width) + (ce >= 2 * width);
+                        char* p = static_cast<char*>(seg == 0 ? out.p[0] : (seg == 1 ? out.p[1] : out.p[2]));
+                        char* d = p + (row * width + (ce - seg * width)) * kYB;
+                        if (Y_BF16)
+                            *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(src + e * kYB);
+                        else
+                            *reinterpret_cast<float*>(d) = *reinterpret_cast<const float*>(src + e * kYB);
+                    }
+                }
+            }
+            }
+        }
+        if (!more) return false;
+        __syncthreads();
+        blk = nxt;
+        return true;
+    };
+    for (;;) {
+        if (!step(rb0, xs[0], xs[1])) break;
+        if (!step(rb1, xs[1], xs[0])) break;
+    }
+}
+
+template <bool XF32, bool Y_BF16>
+hipError_t launch_wstat(const void* x, const uint16_t* w, const float* bias, int64_t M, int K, int N,
+                        const LinearOut& out, hipStream_t stream) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int n_col_blocks = (N + kWsCols - 1) / kWsCols;
+    const int64_t n_row_blocks = (M + ws_rows<XF32>() - 1) / ws_rows<XF32>();
+    int64_t n_streams = cus / n_col_blocks;
+    if (n_streams < 1) n_streams = 1;
+    if (n_streams > n_row_blocks) n_streams = n_row_blocks;
+    const int64_t grid = n_streams * n_col_blocks;
+    // 16-byte stores need pieces that do not straddle output arrays, and aligned arrays (1); the
+    // buffer stores also need each workgroup's 256 columns inside one array (2)
+    const int n_out = N / out.width;
+    bool aligned = true;
+    for (int s = 0; s < n_out; ++s) aligned = aligned && reinterpret_cast<uintptr_t>(out.p[s]) % 16 == 0;
+    const int vec = !aligned ? 0 : out.width % kWsCols == 0 ? 2 : out.width % (Y_BF16 ? 8 : 4) == 0 ? 1 : 0;
+    if (vec == 2)
+        hipLaunchKernelGGL((linear_wstat_kernel<XF32, Y_BF16, true>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(kWsThreads), 0, stream, x, w, bias, M, K, N, out, n_col_blocks, n_streams,
+                           n_row_blocks, vec);
+    else
+        hipLaunchKernelGGL((linear_wstat_kernel<XF32, Y_BF16, false>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(kWsThreads), 0, stream, x, w, bias, M, K, N, out, n_col_blocks, n_streams,
+                           n_row_blocks, vec);
+    return hipGetLastError();
+}
+
 template <typename XPanel, typename XT, bool Y_BF16>
 hipError_t launch_typed(const void* x, const uint16_t* w, const float* bias, int64_t M, int K, int N,
                         const LinearOut& out, hipStream_t stream) {
@@ -190,6 +522,13 @@ hipError_t launch_typed(const void* x, const uint16_t* w, const float* bias, int
 hipError_t launch_linear(const void* x, bool x_bf16, const uint16_t* w, const float* bias, int64_t M, int K, int N,
                          const LinearOut& out, bool y_bf16, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
+    if (K <= kWsK) {
+        if (x_bf16)
+            return y_bf16 ? launch_wstat<false, true>(x, w, bias, M, K, N, out, stream)
+                          : launch_wstat<false, false>(x, w, bias, M, K, N, out, stream);
+        return y_bf16 ? launch_wstat<true, true>(x, w, bias, M, K, N, out, stream)
+                      : launch_wstat<true, false>(x, w, bias, M, K, N, out, stream);
+    }
     if (x_bf16)
         return y_bf16 ? launch_typed<PanelBf16, uint16_t, true>(x, w, bias, M, K, N, out, stream)
                       : launch_typed<PanelBf16, uint16_t, false>(x, w, bias, M, K, N, out, stream);
