@@ -25,6 +25,7 @@ the SDDMM alone and its roofline is the SDDMM's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c5|c3|c2|c1] [--batch B]
                        [--backward]
+       python bench.py --workload relation|projection   # the dense l2_p4 block / the projections
        python bench.py --mode copy      # plain-copy calibration target for the counters
 """
 from __future__ import annotations
@@ -255,6 +256,109 @@ def bench_relation(args, gat, G):
     }))
 
 
+def bench_projection(args, gat, G):
+    """The node projections around the power-law layer (2^20 rows, model dimension 4 x 64 = 256).
+    One step = q/k/v projection (bf16 node rows -> three bf16 [rows, 4, 64] arrays, one call),
+    the graph attention layer on them (fused SDDMM + softmax + aggregation, degree-binning plan
+    built outside the step), and the output projection of the layer's fp32 output (+ bias, fp32)."""
+    import torch
+    p = G.PROJECTION
+    M, K, H, D = p["M"], p["K"], p["heads"], p["head_dim"]
+    w = G.WORKLOADS["c4"]
+    g = G.make_graph(w, args.seed)
+    x, wqkv, _ = G.make_linear(M, K, 3 * K, seed=args.seed, x_dtype="bf16", bias=False)
+    _, wo, bo = G.make_linear(1, K, K, seed=args.seed + 1)
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    xd, wqkvd, wod, bod = t(x), t(wqkv), t(wo), t(bo)
+    rp, col = t(g.row_ptr), t(g.col_idx)
+    E = g.n_edges
+    qkv = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    o = torch.empty((M, H, D), dtype=torch.float32, device=dev)
+    y = [torch.empty((M, K), dtype=torch.float32, device=dev)]
+    plan = gat.gat_plan_build(rp, E, H, D)
+    scale = 1.0 / np.sqrt(D)
+    stream = torch.cuda.current_stream()
+
+    def qkv_proj():
+        gat.gat_linear(xd, wqkvd, n_out=3, y_dtype=torch.bfloat16, out=qkv)
+
+    def layer():
+        gat.gat_fused_layer(rp, col, qkv[2].view(M, H, D), q=qkv[0].view(M, H, D), k=qkv[1].view(M, H, D),
+                            scale=scale, out=o, plan=plan)
+
+    def out_proj():
+        gat.gat_linear(o.view(M, K), wod, bod, out=y)
+
+    def step():
+        qkv_proj()
+        layer()
+        out_proj()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    reps = max(args.steps, 5)
+    t_qkv, t_layer, t_out = timed(qkv_proj, reps), timed(layer, reps), timed(out_proj, reps)
+    bytes_qkv = M * K * 2 + 3 * K * K * 2 + 3 * M * K * 2            # x, w, q/k/v (bf16)
+    bytes_out = M * K * 4 + K * K * 2 + K * 4 + M * K * 4             # o (fp32), w, bias, y (fp32)
+    flops_qkv, flops_out = 2 * M * 3 * K * K, 2 * M * K * K
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        orc = oracle.get()
+        rows, reps_c = 4096, 0
+        xs = x[:rows]
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < 5.0:
+            orc.linear(xs, wqkv)
+            orc.linear(xs, wo, bo.astype(np.float64))
+            reps_c += 1
+        dt = (time.perf_counter() - t1) / reps_c
+        cpu = {"value": rows / dt, "unit": "rows/s (both projections)", "cores": orc.num_threads(),
+               "kind": "oracle", "host": host_cpu(),
+               "sample": f"the q/k/v and output projections of the first {rows} rows, {reps_c} repetitions "
+                         f"(the layer between them is the oracle's layer, measured by the default workload)"}
+    print(json.dumps({
+        "metric": "projected graph attention layer (q/k/v projection, layer, output projection): node rows/s",
+        "value": M / (elapsed / args.steps), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"projections around the c4 layer: {M} rows, {K} -> 3 x {K} (bf16) and "
+                               f"{K} -> {K} (fp32), {H} heads x {D}, {E} edges", "rows": M, "in_dim": K,
+                   "heads": H, "head_dim": D, "n_edges": E, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": bytes_qkv / t_qkv / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": bytes_qkv / t_qkv / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "linear_wstat_kernel, q/k/v projection (bf16 MFMA 32x32x16, fp32 sums)"},
+        "cpu_baseline": cpu,
+        "extra": {"t_qkv_us": t_qkv * 1e6, "t_layer_us": t_layer * 1e6, "t_out_us": t_out * 1e6,
+                  "qkv_bytes": bytes_qkv, "out_bytes": bytes_out,
+                  "qkv_mfma_tflops": flops_qkv / t_qkv / 1e12, "qkv_mfma_frac": flops_qkv / t_qkv / 1e12 / 2500.0,
+                  "out_gbs": bytes_out / t_out / 1e9, "out_frac": bytes_out / t_out / 1e9 / HBM_PEAK_GBS,
+                  "out_mfma_tflops": flops_out / t_out / 1e12},
+    }))
+
+
 def bench_coo(args, w, gat, G):
     """COO workload: one step = one SDDMM over the edge list."""
     import torch
@@ -316,7 +420,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "relation"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "relation", "projection"])
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
@@ -347,6 +451,9 @@ def main():
 
     if args.workload == "relation":
         bench_relation(args, gat, G)
+        return
+    if args.workload == "projection":
+        bench_projection(args, gat, G)
         return
     w = G.WORKLOADS[args.workload]
     if w.kind == "coo":
