@@ -432,7 +432,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the row range would "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the row range would "
               "shard across GPUs after an all-gather of the feature tables). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

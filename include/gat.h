@@ -182,7 +182,7 @@ size_t gat_plan_sizeof(void);
 
 /*
  * Batch of B CSR graphs as one block-diagonal CSR, assembled on the device.  The l2_p37 page
- * judges its 384-node problem too small for the launch overhead; batched, any number of such graphs
+ * finds its 384-node problem too small for the launch overhead; batched, any number of such graphs
  * is one graph, every entry point above covers the batch in the launches of one call, and each
  * row's result is the same as in its own graph (bit for bit: a row only meets its own edges).
  * Inputs (device, int32): the B graphs' own arrays concatenated -- local_row_ptr [sum_b (N_b+1)]

@@ -1,6 +1,6 @@
 // A batch of CSR graphs as one block-diagonal CSR.
 //
-// Small graphs (the 384-node problem of POPCORNBENCH l2_p37, whose work the page judges too small
+// Small graphs (the 384-node problem of POPCORNBENCH l2_p37, whose work the page finds too small
 // for the launch overhead) are launch-bound one at a time.  Stacked block-diagonally -- rows,
 // edges and sources of graph b shifted by the totals of graphs 0..b-1 -- any number of them is one
 // graph, and every entry point then covers the whole batch in the launches of a single call.  Each
