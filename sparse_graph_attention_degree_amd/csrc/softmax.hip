@@ -14,9 +14,13 @@
 //    short_max): a 32-lane slot per row reads the row 32 values at a time (lane q:
 //    edge q/H, head q%H), per-head max / sum are xor-shuffle trees over lanes q,
 //    q^H, q^2H, ...; three passes: max, sum of exp, write.
-//  * long rows: a workgroup per row, the row held in registers across the
-//    workgroup (one coalesced read, one coalesced write); hub rows: segments across
-//    workgroups whose (max, sum) states merge before alpha is written.
+//  * long rows and hub segments (the plan's segment table): a wave per segment,
+//    streaming it in 1024-float chunks with a running (max, sum) per head; a row of
+//    one chunk is written from registers.  Hub rows: their segments' (max, sum)
+//    states merge, then a workgroup per segment writes alpha.
+// Each (row, head) is reduced in an order fixed by the row alone, so a row's
+// result does not depend on the rows around it (a batch of graphs gives every
+// graph's rows the same bits as the graph alone).
 #include <math.h>
 
 #include "kernels.hpp"
@@ -28,6 +32,19 @@ namespace {
 constexpr int kSmG = 32;                       // lanes per row slot
 constexpr int kSmP = kWave / kSmG;             // rows per wave step
 constexpr int kSmRowsPerWave = 32;
+
+// A raw buffer over [p, p + bytes): a load past the end reads 0 without touching memory and a
+// store past it is dropped, so a partial tail needs no per-lane branch.  Each access takes one
+// 32-bit lane offset plus a scalar offset, instead of a 64-bit address per access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const float* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, float v, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
 
 template <int H>
 struct SmSlot {
@@ -83,6 +100,24 @@ __global__ __launch_bounds__(kBlock) void softmax_short_kernel(const int32_t* __
     }
 }
 
+// Loads a run of cn floats into v: v[k] = element lane + 64k, 0 past the end.  The loads go out
+// in groups of 8 under one scalar test each, with no use of a loaded value in between, so all of
+// them are in flight at once.
+template <int N>
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t src, int cn, int lane, float (&v)[N]) {
+    static_assert(N % 8 == 0, "groups of 8");
+#pragma unroll
+    for (int g = 0; g < N; g += 8) {
+        if (g * kWave < cn) {
+#pragma unroll
+            for (int k = g; k < g + 8; ++k) v[k] = bload(src, lane * 4, k * kWave * 4);
+        } else {
+#pragma unroll
+            for (int k = g; k < g + 8; ++k) v[k] = 0.f;
+        }
+    }
+}
+
 constexpr int kBlkRows = 64;       // rows per wave (at most: fewer on graphs too small to fill the device)
 constexpr int64_t kSmFillWaves = 2048;
 constexpr int kBlkBudget = 2048;   // floats staged per wave (8 KB)
@@ -121,18 +156,19 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         const uint64_t nofit = ~fits & (jb < 64 ? (1ull << jb) - 1 : ~0ull) & ~((1ull << i) - 1);
         const int j = nofit ? __builtin_ctzll(nofit) : jb;
         const int last = shfl(re, j - 1);
-        const int len = (last - base) * H;   // floats in the group, <= kBlkBudget
-        const float* src = sc + (int64_t)base * H;
-        float* dst = out + (int64_t)base * H;
+        // floats in the group, <= kBlkBudget (scalar: the buffer descriptors are built from it)
+        const int len = __builtin_amdgcn_readfirstlane((last - base) * H);
+        const int64_t run0 = (int64_t)__builtin_amdgcn_readfirstlane(base) * H;
+        const __amdgpu_buffer_rsrc_t src = span(sc + run0, (int64_t)len * 4);
+        const __amdgpu_buffer_rsrc_t dst = span(out + run0, (int64_t)len * 4);
         // stage the run (all loads issued before the first LDS write)
         float v[kBlkBudget / kWave];
+        load_run(src, len, lane, v);
 #pragma unroll
         for (int t = 0; t < kBlkBudget / kWave; ++t)
-            if (t * kWave < len && t * kWave + lane < len) v[t] = src[t * kWave + lane];
-#pragma unroll
-        for (int t = 0; t < kBlkBudget / kWave; ++t)
-            if (t * kWave < len && t * kWave + lane < len) stage[t * kWave + lane] = v[t];
-        // one lane per (row, head)
+            if (t * kWave < len) stage[t * kWave + lane] = v[t];
+        // one lane per (row, head); the exponentials of the sum pass are kept in the stage and
+        // scaled in place
         const int pairs = (j - i) * H;
         for (int t = 0; t * kWave < pairs; ++t) {
             const int pp = t * kWave + lane;
@@ -146,110 +182,98 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 for (int x = b; x < e; ++x) m = fmaxf(m, stage[x * H + h]);
                 float z = 0.f;
 #pragma unroll 8
-                for (int x = b; x < e; ++x) z += exp_fast(stage[x * H + h] - m);
+                for (int x = b; x < e; ++x) {
+                    const float ex = exp_fast(stage[x * H + h] - m);
+                    stage[x * H + h] = ex;
+                    z += ex;
+                }
                 const float rz = 1.f / z;
 #pragma unroll 8
-                for (int x = b; x < e; ++x) stage[x * H + h] = exp_fast(stage[x * H + h] - m) * rz;
+                for (int x = b; x < e; ++x) stage[x * H + h] *= rz;
             }
         }
 #pragma unroll
         for (int t = 0; t < kBlkBudget / kWave; ++t)
-            if (t * kWave < len && t * kWave + lane < len) dst[t * kWave + lane] = stage[t * kWave + lane];
+            if (t * kWave < len) bstore(dst, stage[t * kWave + lane], lane * 4, t * kWave * 4);
         i = j;
     }
 }
 
-constexpr int kSegRegs = 32;                     // floats each thread holds of a segment
-constexpr int kSegBudget = kSegRegs * kBlock;     // 8192: segments up to this many floats stay in registers
+constexpr int kSegRegs = 16;                      // floats each lane holds of a segment chunk
+constexpr int kWaveChunk = kSegRegs * kWave;       // 1024 floats per chunk
 
-// One workgroup per plan segment.  A segment of up to kSegBudget floats is read once, with
-// coalesced loads, into registers: thread t holds elements t, t+256, ... which all belong to
-// head t % H (256 is a multiple of H), so per-head max and sum are a per-thread pass, an
-// xor-shuffle tree over lanes of one head, and a 4-wave merge through LDS; alpha is then
-// written from the registers.  Longer segments fall back to 8 slots (three passes each).
-// Long rows are written here; hub segments leave (max[H], sum[H]) in the partial buffer.
+// One wave per plan segment (long rows, and hub segments whose (max, sum) states merge
+// afterwards), with no barrier and no LDS, so every wave of the device streams a segment of its
+// own.  A segment is read in chunks of kWaveChunk floats, kSegRegs per lane with coalesced
+// loads: lane l holds elements l, l+64, ... of the chunk, all of head l % H (64 is a multiple of
+// H, and every chunk starts on an edge and holds at least one element of every head).  Per chunk
+// the head's maximum is an xor-shuffle tree over the head's lanes; each lane keeps a running sum
+// of exp(s - max), rescaled when the maximum grows, and the sums of a head meet in a second
+// tree at the end.  A segment of one chunk stays in registers from the read to the write; a
+// longer long row is read again to write alpha.  Hub segments leave (max[H], sum[H]) in their
+// partial slot.
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc, float* out, PlanView plan) {
-    constexpr int NS = kBlock / kSmG;
-    __shared__ float lm[NS][H], lz[NS][H], gm[H], gz[H];
     const int lane = lane_id();
-    const int t = threadIdx.x;
-    const int w = t / kWave;
-    const int gs = t / kSmG;
-    SmSlot<H> sl;
-    sl.q = lane % kSmG;
-    const int n_segs = plan.counts[kNSegs];
-    for (int s = blockIdx.x; s < n_segs; s += gridDim.x) {
+    const int64_t n_segs = plan.counts[kNSegs];
+    const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
+    // the wave index as a scalar, so that the segment entry and the buffer descriptors built
+    // from it stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave; s < n_segs; s += n_waves) {
         const int4 sg = plan.segs[s];
-        const int64_t len = (int64_t)sg.z - sg.y;
-        if (len * H <= kSegBudget) {
-            const int n = (int)len * H;
-            const int64_t off = (int64_t)sg.y * H;
-            float v[kSegRegs];
-            float m = -INFINITY;
+        const int64_t n = (int64_t)(sg.z - sg.y) * H;
+        const float* seg = sc + (int64_t)sg.y * H;
+        float v[kSegRegs];
+        float m = -INFINITY, z = 0.f;
+        for (int64_t c0 = 0; c0 < n; c0 += kWaveChunk) {
+            const int cn = (int)(n - c0 < kWaveChunk ? n - c0 : kWaveChunk);
+            const __amdgpu_buffer_rsrc_t src = span(seg + c0, (int64_t)cn * 4);
+            load_run(src, cn, lane, v);
+            float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k) {
-                v[k] = -INFINITY;
-                if (k * kBlock < n && t + k * kBlock < n) v[k] = sc[off + t + k * kBlock];
-                m = fmaxf(m, v[k]);
+                if (lane >= cn - k * kWave) v[k] = -INFINITY;   // scalar bound: no per-k lane index kept
+                cm = fmaxf(cm, v[k]);
             }
 #pragma unroll
-            for (int o = H; o < kWave; o <<= 1) m = fmaxf(m, shfl_xor(m, o));
-            if (lane < H) lm[w][lane] = m;
-            __syncthreads();
-            const int h = t % H;
-            float M = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < kWavesPerBlock; ++i) M = fmaxf(M, lm[i][h]);
-            float z = 0.f;
+            for (int o = H; o < kWave; o <<= 1) cm = fmaxf(cm, shfl_xor(cm, o));
+            const float mn = fmaxf(m, cm);   // finite: the chunk holds an element of this head
+            float cz = 0.f;
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k)
-                if (k * kBlock < n && t + k * kBlock < n) z += exp_fast(v[k] - M);
+                if (k * kWave < cn) cz += exp_fast(v[k] - mn);   // exp(-inf) = 0 past the end
+            z = z * exp_fast(m - mn) + cz;                         // m = -inf on the first chunk: z = cz
+            m = mn;
+        }
 #pragma unroll
-            for (int o = H; o < kWave; o <<= 1) z += shfl_xor(z, o);
-            if (lane < H) lz[w][lane] = z;
-            __syncthreads();
-            float Z = 0.f;
-#pragma unroll
-            for (int i = 0; i < kWavesPerBlock; ++i) Z += lz[i][h];
-            if (sg.w < 0) {
-                const float rz = 1.f / Z;
-#pragma unroll
-                for (int k = 0; k < kSegRegs; ++k)
-                    if (k * kBlock < n && t + k * kBlock < n) out[off + t + k * kBlock] = exp_fast(v[k] - M) * rz;
-            } else if (t < H) {
+        for (int o = H; o < kWave; o <<= 1) z += shfl_xor(z, o);
+        if (sg.w >= 0) {
+            if (lane < H) {
                 float* prt = plan.partials + (int64_t)sg.w * plan.state_floats;
-                prt[t] = M;
-                prt[H + t] = Z;
+                prt[lane] = m;
+                prt[H + lane] = z;
             }
-            __syncthreads();
             continue;
         }
-        const int b = sg.y + (int)(len * gs / NS), e = sg.y + (int)(len * (gs + 1) / NS);
-        float m, z;
-        sl.stats(sc, b, e, m, z);
-        if (sl.q < H) {
-            lm[gs][sl.q] = m;
-            lz[gs][sl.q] = z;
+        const float rz = 1.f / z;
+        float* dseg = out + (int64_t)sg.y * H;
+        if (n <= kWaveChunk) {
+            const __amdgpu_buffer_rsrc_t dst = span(dseg, n * 4);
+#pragma unroll
+            for (int k = 0; k < kSegRegs; ++k)
+                if (k * kWave < n) bstore(dst, exp_fast(v[k] - m) * rz, lane * 4, k * kWave * 4);
+            continue;
         }
-        __syncthreads();
-        if (threadIdx.x < H) {
-            const int h = threadIdx.x;
-            float M = -INFINITY, Z = 0.f;
-            for (int i = 0; i < NS; ++i) M = fmaxf(M, lm[i][h]);
-            for (int i = 0; i < NS; ++i)
-                if (lm[i][h] != -INFINITY) Z = fmaf(lz[i][h], exp_fast(lm[i][h] - M), Z);
-            gm[h] = M;
-            gz[h] = Z;
-            if (sg.w >= 0) {
-                float* prt = plan.partials + (int64_t)sg.w * plan.state_floats;
-                prt[h] = M;
-                prt[H + h] = Z;
-            }
+        for (int64_t c0 = 0; c0 < n; c0 += kWaveChunk) {
+            const int cn = (int)(n - c0 < kWaveChunk ? n - c0 : kWaveChunk);
+            const __amdgpu_buffer_rsrc_t src = span(seg + c0, (int64_t)cn * 4);
+            const __amdgpu_buffer_rsrc_t dst = span(dseg + c0, (int64_t)cn * 4);
+            load_run(src, cn, lane, v);
+#pragma unroll
+            for (int k = 0; k < kSegRegs; ++k)
+                if (k * kWave < cn) bstore(dst, exp_fast(v[k] - m) * rz, lane * 4, k * kWave * 4);
         }
-        __syncthreads();
-        if (sg.w < 0) sl.write(sc, out, b, e, gm[sl.q % H], gz[sl.q % H]);
-        __syncthreads();
     }
 }
 
@@ -311,7 +335,13 @@ __global__ __launch_bounds__(kBlock) void softmax_hub_merge_kernel(PlanView plan
     }
 }
 
-// One workgroup per hub segment: read the row's merged state, then write alpha.
+// One workgroup per hub segment: read the row's merged state, then write alpha.  The scores of
+// a segment are read in batches of kHubBatch elements per thread, all loads of a batch issued
+// before the first store (out may alias sc, so the compiler would otherwise keep each
+// load-exp-store in order).  The batch loads do not depend on the merged state, so they are
+// issued before it is fetched.
+constexpr int kHubBatch = 16;
+
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_hub_write_kernel(const int32_t* __restrict__ row_ptr,
                                                                    const float* sc, float* out, PlanView plan) {
@@ -323,9 +353,21 @@ __global__ __launch_bounds__(kBlock) void softmax_hub_write_kernel(const int32_t
         const float* p0 = plan.partials + (int64_t)first * plan.state_floats;
         // kBlock is a multiple of H, so every element this thread touches has head t % H
         const int h = threadIdx.x % H;
-        const float M = p0[h], rz = 1.f / p0[H + h];
-        for (int64_t i = (int64_t)sg.y * H + threadIdx.x; i < (int64_t)sg.z * H; i += kBlock)
-            out[i] = exp_fast(sc[i] - M) * rz;
+        const int64_t end = (int64_t)sg.z * H;
+        for (int64_t i0 = (int64_t)sg.y * H + threadIdx.x; i0 < end; i0 += kHubBatch * kBlock) {
+            float v[kHubBatch];
+#pragma unroll
+            for (int k = 0; k < kHubBatch; ++k) {
+                const int64_t i = i0 + (int64_t)k * kBlock;
+                v[k] = i < end ? sc[i] : 0.f;
+            }
+            const float M = p0[h], rz = 1.f / p0[H + h];
+#pragma unroll
+            for (int k = 0; k < kHubBatch; ++k) {
+                const int64_t i = i0 + (int64_t)k * kBlock;
+                if (i < end) out[i] = exp_fast(v[k] - M) * rz;
+            }
+        }
     }
 }
 
@@ -338,7 +380,8 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         const int short_max = plan ? plan->short_max : INT32_MAX;
         const int staged = short_max < kBlkBudget / HH ? short_max : kBlkBudget / HH;   // rows the stage takes
         if (plan)
-            hipLaunchKernelGGL(softmax_segment_kernel<HH>, dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)),
+            hipLaunchKernelGGL(softmax_segment_kernel<HH>,
+                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kPersistentBlocks)),
                                dim3(kBlock), 0, stream, scores, out, *plan);
         int64_t rpw = (n_rows + kSmFillWaves - 1) / kSmFillWaves;   // enough waves to fill the device
         rpw = rpw < 1 ? 1 : (rpw > kBlkRows ? kBlkRows : rpw);
