@@ -5,7 +5,7 @@
 // The page's kernels map one thread to a (node, head) pair striding through the
 // slice with stride H, or one block per node with shared-memory reductions.
 // Here, by degree:
-//  * short rows (the common case): a wave takes 64 consecutive rows; their scores
+//  * short rows (the common case): a wave takes 32 consecutive rows; their scores
 //    form one contiguous run, which the wave stages into LDS with coalesced loads
 //    (up to kBlkBudget floats at a time, whole rows).  One lane per (row, head)
 //    then computes max, sum of exp and alpha from LDS, and the wave streams alpha
@@ -118,11 +118,11 @@ __device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t src, int cn, int
     }
 }
 
-constexpr int kBlkRows = 64;       // rows per wave (at most: fewer on graphs too small to fill the device)
+constexpr int kBlkRows = 32;       // rows per wave (at most: fewer on graphs too small to fill the device)
 constexpr int64_t kSmFillWaves = 2048;
-constexpr int kBlkBudget = 2048;   // floats staged per wave (8 KB)
+constexpr int kBlkBudget = 1024;   // floats staged per wave (4 KB: 16 KB per workgroup, so LDS admits 10)
 
-// Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per 64 consecutive rows, groups of
+// Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per 32 consecutive rows, groups of
 // consecutive such rows staged in LDS.  A row of another class (non-empty, deg > hi) ends a
 // group, since its scores sit between the groups' runs.
 template <int H>
