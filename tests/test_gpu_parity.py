@@ -130,6 +130,33 @@ def test_edge_softmax(orc, H, sched):
     assert np.array_equal(to_np(inplace), to_np(out))
 
 
+@pytest.mark.parametrize("H", [1, 4, 8, 16])
+@pytest.mark.parametrize("seg_len", [5000, 1024, 129, 100])
+def test_edge_softmax_chunk_boundaries(orc, H, seg_len):
+    """Long rows and hub segments whose score runs end on, just before and just past the 1024-float
+    chunks the segment kernel streams (a one-chunk row is written from registers, longer ones are
+    read again), with a trend along each row so the running maximum grows from chunk to chunk (or
+    never does); out of place and in place."""
+    degs = []
+    for n in (1024, 2048, 3072, 4096):
+        degs += [max(1, n // H - 1), n // H, n // H + 1]
+    degs = np.array(degs + [0, 1, 3, 0, 7], dtype=np.int64)
+    r = np.random.default_rng(31 + H)
+    r.shuffle(degs)
+    g = G.csr_from_degrees(degs, 700, r)
+    s = (r.standard_normal((g.n_edges, H)) * 2).astype(np.float64)
+    for i in range(g.n_rows):
+        b, e = g.row_ptr[i], g.row_ptr[i + 1]
+        s[b:e] += np.linspace(0.0, 12.0 if i % 2 else -12.0, e - b)[:, None]
+    s = s.astype(np.float32)
+    rp, sd = to_dev(g.row_ptr), to_dev(s)
+    plan = gat.gat_plan_build(rp, g.n_edges, H, 16, short_max=0, seg_len=seg_len)
+    out = gat.gat_edge_softmax(rp, sd, plan=plan)
+    assert_close(to_np(out), orc.edge_softmax(g.row_ptr, s), "f32", f"edge softmax, seg_len {seg_len}")
+    inplace = gat.gat_edge_softmax(rp, sd, out=sd, plan=plan)
+    assert np.array_equal(to_np(inplace), to_np(out))
+
+
 @pytest.mark.parametrize("H,D,dt", SHAPES)
 def test_sddmm(orc, H, D, dt):
     r = np.random.default_rng(10)
