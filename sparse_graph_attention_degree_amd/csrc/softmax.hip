@@ -336,25 +336,57 @@ __global__ __launch_bounds__(kBlock) void softmax_hub_merge_kernel(PlanView plan
 }
 
 // One workgroup per hub segment: read the row's merged state, then write alpha.  The scores of
-// a segment are read in batches of kHubBatch elements per thread, all loads of a batch issued
-// before the first store (out may alias sc, so the compiler would otherwise keep each
-// load-exp-store in order).  The batch loads do not depend on the merged state, so they are
-// issued before it is fetched.
-constexpr int kHubBatch = 16;
+// a segment are read in batches, all loads of a batch issued before the first store (out may
+// alias sc, so the compiler would otherwise keep each load-exp-store in order).  The batch loads
+// do not depend on the merged state, so they are issued before it is fetched.  With H >= 4 and
+// 16-byte aligned arrays a segment's run starts on a 16-byte boundary, and threads move 4
+// consecutive floats at a time (heads (4t + j) % H, fixed per thread since 1024 is a multiple
+// of H); otherwise one float at a time.
+constexpr int kHubBatch = 16;   // floats per thread per batch
 
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_hub_write_kernel(const int32_t* __restrict__ row_ptr,
                                                                    const float* sc, float* out, PlanView plan) {
     const int n_hub_segs = plan.counts[kNHubSegs];
+    const bool wide = H >= 4 && ((reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
     for (int s = blockIdx.x; s < n_hub_segs; s += gridDim.x) {
         const int4 sg = plan.segs[s];   // row, b, e, slot (= s)
         const int rb = row_ptr[sg.x];
         const int first = sg.w - (int)(((int64_t)sg.y - rb) / plan.seg_len);
         const float* p0 = plan.partials + (int64_t)first * plan.state_floats;
+        const int64_t beg = (int64_t)sg.y * H, end = (int64_t)sg.z * H;
+        if (wide) {
+            constexpr int NB = kHubBatch / 4;   // float4 per thread per batch
+            const float4* s4 = reinterpret_cast<const float4*>(sc + beg);
+            float4* o4 = reinterpret_cast<float4*>(out + beg);
+            const int64_t n4 = (end - beg) / 4;   // H >= 4: whole float4s
+            for (int64_t f0 = threadIdx.x; f0 < n4; f0 += NB * kBlock) {
+                float4 v[NB];
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const int64_t f = f0 + (int64_t)k * kBlock;
+                    v[k] = f < n4 ? s4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                const int h0 = (4 * threadIdx.x) % H;
+                float M[4], rz[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    M[j] = p0[(h0 + j) % H];
+                    rz[j] = 1.f / p0[H + (h0 + j) % H];
+                }
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const int64_t f = f0 + (int64_t)k * kBlock;
+                    if (f < n4)
+                        o4[f] = make_float4(exp_fast(v[k].x - M[0]) * rz[0], exp_fast(v[k].y - M[1]) * rz[1],
+                                            exp_fast(v[k].z - M[2]) * rz[2], exp_fast(v[k].w - M[3]) * rz[3]);
+                }
+            }
+            continue;
+        }
         // kBlock is a multiple of H, so every element this thread touches has head t % H
         const int h = threadIdx.x % H;
-        const int64_t end = (int64_t)sg.z * H;
-        for (int64_t i0 = (int64_t)sg.y * H + threadIdx.x; i0 < end; i0 += kHubBatch * kBlock) {
+        for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += kHubBatch * kBlock) {
             float v[kHubBatch];
 #pragma unroll
             for (int k = 0; k < kHubBatch; ++k) {
