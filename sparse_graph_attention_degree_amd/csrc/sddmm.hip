@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t* __restrict
                                                        float scale, float* __restrict__ out) {
     using Gm = Geo<T, H, D>;
     constexpr int G = Gm::G, P = Gm::P, NV = Gm::NV, EPP = Gm::EPP, LPH = Gm::LPH, HD = Gm::HD;
-    constexpr int UMAX = (4 / NV) > 1 ? (4 / NV) : 1;
+    constexpr int UMAX = (8 / NV) > 1 ? (8 / NV) : 1;   // up to 8 pieces of each row in flight per lane
     constexpr int U = UMAX * P <= kWave ? UMAX : kWave / P;
     constexpr int EPI = U * P;   // edges per wave iteration (<= 64: one index per lane)
     const int lane = lane_id();
@@ -88,7 +88,7 @@ hipError_t launch_sddmm(int dtype, int H, int D, const int32_t* src_idx, const i
         using Tag = decltype(tag);
         using T = typename Tag::type;
         using Gm = Geo<T, Tag::H, Tag::D>;
-        constexpr int UMAX = (4 / Gm::NV) > 1 ? (4 / Gm::NV) : 1;
+        constexpr int UMAX = (8 / Gm::NV) > 1 ? (8 / Gm::NV) : 1;
         constexpr int U = UMAX * Gm::P <= kWave ? UMAX : kWave / Gm::P;
         const int64_t waves = (n_edges + U * Gm::P - 1) / (U * Gm::P);
         hipLaunchKernelGGL((sddmm_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, 65536)),
