@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include "kernels.hpp"
+#include "span.hpp"
 
 namespace gat {
 
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kBlock) void edge_dot_kernel(const int32_t* __restr
                                                           float* __restrict__ out) {
     using Gm = Geo<T, H, D>;
     constexpr int G = Gm::G, P = Gm::P, NV = Gm::NV, EPP = Gm::EPP, LPH = Gm::LPH, HD = Gm::HD;
-    constexpr int UMAX = (4 / NV) > 1 ? (4 / NV) : 1;
+    constexpr int UMAX = (8 / NV) > 1 ? (8 / NV) : 1;   // up to 8 pieces of each row in flight per lane
     constexpr int U = UMAX * P <= kWave ? UMAX : kWave / P;
     constexpr int EPI = U * P;   // edges per wave iteration (<= 64: one index per lane)
     const int lane = lane_id();
@@ -315,6 +316,7 @@ __global__ __launch_bounds__(kBlock) void edge_dot_kernel(const int32_t* __restr
 constexpr int kSbG = 32;                  // lanes per row slot: lane q reads edge q/H, head q%H
 constexpr int kSbRowsPerWave = 32;        // at most; a multiple of the 2 slots per wave
 constexpr int64_t kSbFillWaves = 2048;
+constexpr int kSbRegs = 8;                // rows of up to 8 values per lane are held in registers
 
 // rows with deg <= hi (all rows when there is no plan), a 32-lane slot per row: one pass for the
 // per-head dot, one for the output
@@ -335,6 +337,28 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_short_kernel(const int32_t
         const int j = it * (kWave / kSbG) + g;
         int e0 = shfl(rpv, j), e1 = shfl(rpv, j + 1);
         if (!(wb + j < n_rows && e1 - e0 <= hi)) e1 = e0;
+        if (e1 - e0 <= kSbRegs * SC) {
+            // the row in registers: lane q holds elements q, q+32, ... of its run; all loads are
+            // issued before the first use
+            const int n = (e1 - e0) * H;
+            const int64_t r0 = (int64_t)e0 * H + q;
+            float a[kSbRegs], gr[kSbRegs];
+#pragma unroll
+            for (int k = 0; k < kSbRegs; ++k) {
+                const bool live = q + k * kSbG < n;
+                a[k] = live ? alpha[r0 + k * kSbG] : 0.f;
+                gr[k] = live ? grad[r0 + k * kSbG] : 0.f;
+            }
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < kSbRegs; ++k) s = fmaf(a[k], gr[k], s);
+#pragma unroll
+            for (int o = H; o < kSbG; o <<= 1) s += shfl_xor(s, o);
+#pragma unroll
+            for (int k = 0; k < kSbRegs; ++k)
+                if (q + k * kSbG < n) out[r0 + k * kSbG] = scale * a[k] * (gr[k] - s);
+            continue;
+        }
         float s = 0.f;
         for (int c = e0; c < e1; c += SC)
             if (c + es < e1) {
@@ -366,29 +390,60 @@ __device__ __forceinline__ float block_head_sum(float s, float (*ls)[H]) {
     return t;
 }
 
-// one workgroup per plan segment: thread t takes elements t, t+256, ... (all of head t % H);
-// a long row is written here, a hub segment leaves its per-head dot in the partial buffer
+// One wave per plan segment, no barrier: the segment streams through in 1024-float chunks of
+// alpha and grad (lane l holds elements l, l+64, ..., all of head l % H), the per-head dot is a
+// per-lane sum and an xor-shuffle tree over the head's lanes; a one-chunk long row is written from
+// registers, a longer one is read again; a hub segment leaves its per-head dot in the partial
+// buffer.
+constexpr int kSbSegRegs = 16;
+constexpr int kSbChunk = kSbSegRegs * kWave;
+
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_bwd_segment_kernel(const float* alpha, const float* grad,
                                                                      float* out, PlanView plan, float scale) {
-    __shared__ float ls[kWavesPerBlock][H];
-    const int t = threadIdx.x;
-    const int n_segs = plan.counts[kNSegs];
-    for (int s = blockIdx.x; s < n_segs; s += gridDim.x) {
+    const int lane = lane_id();
+    const int64_t n_segs = plan.counts[kNSegs];
+    const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);   // scalar: see span.hpp
+#pragma unroll 1
+    for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave; s < n_segs; s += n_waves) {
         const int4 sg = plan.segs[s];
-        const int64_t b = (int64_t)sg.y * H, e = (int64_t)sg.z * H;
-        float acc = 0.f;
-        for (int64_t i = b + t; i < e; i += kBlock) acc = fmaf(alpha[i], grad[i], acc);
-        const float dot = block_head_sum<H>(acc, ls);
-        if (sg.w < 0) {
-            for (int64_t i = b + t; i < e; i += kBlock) out[i] = scale * alpha[i] * (grad[i] - dot);
-        } else if (t < H) {
-            plan.partials[(int64_t)sg.w * plan.state_floats + t] = dot;
+        const int64_t n = (int64_t)(sg.z - sg.y) * H;
+        const int64_t off = (int64_t)sg.y * H;
+        float a[kSbSegRegs], g[kSbSegRegs];
+        float dot = 0.f;
+#pragma unroll 1
+        for (int64_t c0 = 0; c0 < n; c0 += kSbChunk) {
+            const int cn = (int)(n - c0 < kSbChunk ? n - c0 : kSbChunk);
+            load_run(span(alpha + off + c0, (int64_t)cn * 4), cn, lane, a);
+            load_run(span(grad + off + c0, (int64_t)cn * 4), cn, lane, g);
+#pragma unroll
+            for (int k = 0; k < kSbSegRegs; ++k) dot = fmaf(a[k], g[k], dot);   // 0 past the end
+        }
+#pragma unroll
+        for (int o = H; o < kWave; o <<= 1) dot += shfl_xor(dot, o);
+        if (sg.w >= 0) {
+            if (lane < H) plan.partials[(int64_t)sg.w * plan.state_floats + lane] = dot;
+            continue;
+        }
+#pragma unroll 1
+        for (int64_t c0 = 0; c0 < n; c0 += kSbChunk) {
+            const int cn = (int)(n - c0 < kSbChunk ? n - c0 : kSbChunk);
+            if (n > kSbChunk) {
+                load_run(span(alpha + off + c0, (int64_t)cn * 4), cn, lane, a);
+                load_run(span(grad + off + c0, (int64_t)cn * 4), cn, lane, g);
+            }
+            const __amdgpu_buffer_rsrc_t dst = span(out + off + c0, (int64_t)cn * 4);
+#pragma unroll
+            for (int k = 0; k < kSbSegRegs; ++k)
+                if (k * kWave < cn) bstore(dst, scale * a[k] * (g[k] - dot), lane * 4, k * kWave * 4);
         }
     }
 }
 
 // one workgroup per hub segment: the hub's dot is the sum of its segments' partials
+constexpr int kSbHubBatch = 8;
+
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_bwd_hub_kernel(const int32_t* __restrict__ row_ptr,
                                                                  const float* alpha, const float* grad, float* out,
@@ -406,8 +461,23 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_hub_kernel(const int32_t* 
         for (int c = t / H; c < nseg; c += kBlock / H)
             acc += plan.partials[(int64_t)(first + c) * plan.state_floats + t % H];
         const float dot = block_head_sum<H>(acc, ls);
-        for (int64_t i = (int64_t)sg.y * H + t; i < (int64_t)sg.z * H; i += kBlock)
-            out[i] = scale * alpha[i] * (grad[i] - dot);
+        // batches of kSbHubBatch elements per thread, all loads before the first store (out may
+        // alias grad)
+        const int64_t end = (int64_t)sg.z * H;
+        for (int64_t i0 = (int64_t)sg.y * H + t; i0 < end; i0 += kSbHubBatch * kBlock) {
+            float a[kSbHubBatch], g[kSbHubBatch];
+#pragma unroll
+            for (int k = 0; k < kSbHubBatch; ++k) {
+                const int64_t i = i0 + (int64_t)k * kBlock;
+                a[k] = i < end ? alpha[i] : 0.f;
+                g[k] = i < end ? grad[i] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < kSbHubBatch; ++k) {
+                const int64_t i = i0 + (int64_t)k * kBlock;
+                if (i < end) out[i] = scale * a[k] * (g[k] - dot);
+            }
+        }
     }
 }
 
@@ -475,7 +545,7 @@ hipError_t launch_edge_dot(int dtype, int H, int D, const int32_t* rows, const i
         using Tag = decltype(tag);
         using T = typename Tag::type;
         using Gm = Geo<T, Tag::H, Tag::D>;
-        constexpr int UMAX = (4 / Gm::NV) > 1 ? (4 / Gm::NV) : 1;
+        constexpr int UMAX = (8 / Gm::NV) > 1 ? (8 / Gm::NV) : 1;
         constexpr int U = UMAX * Gm::P <= kWave ? UMAX : kWave / Gm::P;
         const int64_t waves = (n_edges + U * Gm::P - 1) / (U * Gm::P);
         hipLaunchKernelGGL((edge_dot_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, 65536)),
@@ -492,8 +562,8 @@ hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows
         constexpr int HH = decltype(tag)::H;
         if (plan)
             hipLaunchKernelGGL(softmax_bwd_segment_kernel<HH>,
-                               dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
-                               alpha, grad, out, *plan, scale);
+                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kPersistentBlocks)), dim3(kBlock),
+                               0, stream, alpha, grad, out, *plan, scale);
         // rows per wave: a multiple of the slots per wave, small enough to fill the device
         constexpr int slots = kWave / kSbG;
         int64_t rpw = (n_rows + kSbFillWaves - 1) / kSbFillWaves;

@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include "kernels.hpp"
+#include "span.hpp"
 
 namespace gat {
 
@@ -32,19 +33,6 @@ namespace {
 constexpr int kSmG = 32;                       // lanes per row slot
 constexpr int kSmP = kWave / kSmG;             // rows per wave step
 constexpr int kSmRowsPerWave = 32;
-
-// A raw buffer over [p, p + bytes): a load past the end reads 0 without touching memory and a
-// store past it is dropped, so a partial tail needs no per-lane branch.  Each access takes one
-// 32-bit lane offset plus a scalar offset, instead of a 64-bit address per access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const float* p, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, float v, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
-}
 
 template <int H>
 struct SmSlot {
@@ -97,24 +85,6 @@ __global__ __launch_bounds__(kBlock) void softmax_short_kernel(const int32_t* __
         float m, z;
         sl.stats(sc, e0, e1, m, z);
         sl.write(sc, out, e0, e1, m, z);
-    }
-}
-
-// Loads a run of cn floats into v: v[k] = element lane + 64k, 0 past the end.  The loads go out
-// in groups of 8 under one scalar test each, with no use of a loaded value in between, so all of
-// them are in flight at once.
-template <int N>
-__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t src, int cn, int lane, float (&v)[N]) {
-    static_assert(N % 8 == 0, "groups of 8");
-#pragma unroll
-    for (int g = 0; g < N; g += 8) {
-        if (g * kWave < cn) {
-#pragma unroll
-            for (int k = g; k < g + 8; ++k) v[k] = bload(src, lane * 4, k * kWave * 4);
-        } else {
-#pragma unroll
-            for (int k = g; k < g + 8; ++k) v[k] = 0.f;
-        }
     }
 }
 
