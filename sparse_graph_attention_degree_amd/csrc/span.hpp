@@ -11,6 +11,8 @@
 
 namespace gat {
 
+// bytes < 2^31 (the descriptor's record count is 32-bit; every caller passes one run or chunk of at
+// most a few KB)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const float* p, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, (int)bytes, 0x00020000);
 }
