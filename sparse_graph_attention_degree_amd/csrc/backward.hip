@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_segment_kernel(const float
             const __amdgpu_buffer_rsrc_t dst = span(out + off + c0, (int64_t)cn * 4);
 #pragma unroll
             for (int k = 0; k < kSbSegRegs; ++k)
-                if (k * kWave < cn) bstore(dst, scale * a[k] * (g[k] - dot), lane * 4, k * kWave * 4);
+                if (k * kWave < cn) bstore(dst, scale * a[k] * (g[k] - dot), (lane + k * kWave) * 4);
         }
     }
 }

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         }
 #pragma unroll
         for (int t = 0; t < kBlkBudget / kWave; ++t)
-            if (t * kWave < len) bstore(dst, stage[t * kWave + lane], lane * 4, t * kWave * 4);
+            if (t * kWave < len) bstore(dst, stage[t * kWave + lane], (lane + t * kWave) * 4);
         i = j;
     }
 }
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
             const __amdgpu_buffer_rsrc_t dst = span(dseg, n * 4);
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k)
-                if (k * kWave < n) bstore(dst, exp_fast(v[k] - m) * rz, lane * 4, k * kWave * 4);
+                if (k * kWave < n) bstore(dst, exp_fast(v[k] - m) * rz, (lane + k * kWave) * 4);
             continue;
         }
         for (int64_t c0 = 0; c0 < n; c0 += kWaveChunk) {
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
             load_run(src, cn, lane, v);
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k)
-                if (k * kWave < cn) bstore(dst, exp_fast(v[k] - m) * rz, lane * 4, k * kWave * 4);
+                if (k * kWave < cn) bstore(dst, exp_fast(v[k] - m) * rz, (lane + k * kWave) * 4);
         }
     }
 }

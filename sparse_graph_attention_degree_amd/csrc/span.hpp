@@ -4,7 +4,7 @@
 // for every lane of the wave: build it from wave-uniform values, or the compiler wraps each access
 // in a readfirstlane loop).  A load past the end reads 0 without touching memory and a store past
 // it is dropped, so a partial tail needs no per-lane branch; each access costs one 32-bit lane
-// offset plus a scalar offset instead of a 64-bit address.
+// offset (plus an immediate) instead of a 64-bit address.
 #pragma once
 
 #include "common.hpp"
@@ -16,11 +16,14 @@ namespace gat {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const float* p, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+// off: byte offset of this lane's element.  It is passed as the lane offset (with a constant
+// part the compiler folds into the instruction's immediate offset), both of which the range
+// check covers; the scalar offset stays 0.
+__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, float v, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, float v, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
 // Loads a run of cn floats into v: v[k] = element lane + 64k, 0 past the end.  The loads go out
@@ -33,7 +36,7 @@ __device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t src, int cn, int
     for (int g = 0; g < N; g += 8) {
         if (g * kWave < cn) {
 #pragma unroll
-            for (int k = g; k < g + 8; ++k) v[k] = bload(src, lane * 4, k * kWave * 4);
+            for (int k = g; k < g + 8; ++k) v[k] = bload(src, (lane + k * kWave) * 4);
         } else {
 #pragma unroll
             for (int k = g; k < g + 8; ++k) v[k] = 0.f;
