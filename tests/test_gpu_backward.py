@@ -92,6 +92,31 @@ def test_edge_softmax_backward(orc, H, sched):
     assert_close(got, want, "f32", "edge softmax backward")
 
 
+@pytest.mark.parametrize("H", [1, 4, 8, 16])
+@pytest.mark.parametrize("seg_len", [5000, 1024, 129])
+def test_edge_softmax_backward_chunk_boundaries(orc, H, seg_len):
+    """Long rows and hub segments whose alpha/grad runs end on, just before and just past the
+    1024-float chunks the backward segment kernel streams (a one-chunk row is written from
+    registers, longer ones are read again), out of place and in place."""
+    degs = []
+    for n in (1024, 2048, 3072):
+        degs += [max(1, n // H - 1), n // H, n // H + 1]
+    degs = np.array(degs + [0, 1, 3, 0, 7], dtype=np.int64)
+    r = np.random.default_rng(41 + H)
+    r.shuffle(degs)
+    g = G.csr_from_degrees(degs, 600, r)
+    alpha = orc.edge_softmax(g.row_ptr, r.standard_normal((g.n_edges, H)) * 2).astype(np.float32)
+    grad = r.standard_normal((g.n_edges, H)).astype(np.float32)
+    rp = to_dev(g.row_ptr)
+    plan = gat.gat_plan_build(rp, g.n_edges, H, 64, short_max=0, seg_len=seg_len)
+    want = orc.edge_softmax_backward(g.row_ptr, alpha, grad)
+    got = gat.gat_edge_softmax_backward(rp, to_dev(alpha), to_dev(grad), plan=plan)
+    assert_close(to_np(got), want, "f32", f"edge softmax backward, seg_len {seg_len}")
+    gd = to_dev(grad)
+    gat.gat_edge_softmax_backward(rp, to_dev(alpha), gd, out=gd, plan=plan)
+    assert np.array_equal(to_np(gd), to_np(got))
+
+
 def test_edge_softmax_backward_in_place(orc):
     g = mixed_graph(15)
     r = np.random.default_rng(16)
