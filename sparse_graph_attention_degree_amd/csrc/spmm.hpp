@@ -375,7 +375,7 @@ struct Engine {
 // give kFillWaves waves that many rows each (the grid then has one row per slot).  Rows with
 // deg > short_max belong to the segment kernel and are skipped; short_max = INT_MAX without a
 // plan.
-constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerWave = 16;
 constexpr int64_t kFillWaves = 2048;   // 256 CUs x 8 waves
 // Slot width of the short-row kernel (lanes per row in flight).
 constexpr int kShortSlotLanes = 32;
