@@ -562,7 +562,7 @@ hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows
         constexpr int HH = decltype(tag)::H;
         if (plan)
             hipLaunchKernelGGL(softmax_bwd_segment_kernel<HH>,
-                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kPersistentBlocks)), dim3(kBlock),
+                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kSegmentGrid)), dim3(kBlock),
                                0, stream, alpha, grad, out, *plan, scale);
         // rows per wave: a multiple of the slots per wave, small enough to fill the device
         constexpr int slots = kWave / kSbG;
@@ -575,7 +575,7 @@ hipError_t launch_softmax_backward(int H, const int32_t* row_ptr, int64_t n_rows
                            plan ? plan->short_max : INT32_MAX, scale, (int)rpw);
         if (plan)
             hipLaunchKernelGGL(softmax_bwd_hub_kernel<HH>,
-                               dim3(grid_for(plan->hubseg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
+                               dim3(grid_for(plan->hubseg_capacity, 1, kSegmentGrid)), dim3(kBlock), 0, stream,
                                row_ptr, alpha, grad, out, *plan, scale);
     });
     if (!ok) return hipErrorInvalidValue;

@@ -165,6 +165,11 @@ struct PlanView {
 
 // Grid cap of the persistent kernels: 256 CUs x 8 workgroups.
 constexpr int64_t kPersistentBlocks = 2048;
+// Grid cap of the kernels over the plan's segment table (sized by the table's capacity; workgroups
+// past the real count exit at once): up to this many, about one segment (or one hub segment) per
+// workgroup or wave.  Segments differ in length by up to seg_len / short_max, and the hardware
+// dispatcher balances them across the CUs better than a fixed stride over a resident grid.
+constexpr int64_t kSegmentGrid = 65536;
 
 enum CountIdx { kNSegs = 0, kNHubSegs = 1, kNHubs = 2, kNLong = 3 };
 

@@ -383,7 +383,7 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         const int staged = short_max < kBlkBudget / HH ? short_max : kBlkBudget / HH;   // rows the stage takes
         if (plan)
             hipLaunchKernelGGL(softmax_segment_kernel<HH>,
-                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kPersistentBlocks)),
+                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kSegmentGrid)),
                                dim3(kBlock), 0, stream, scores, out, *plan);
         int64_t rpw = (n_rows + kSmFillWaves - 1) / kSmFillWaves;   // enough waves to fill the device
         rpw = rpw < 1 ? 1 : (rpw > kBlkRows ? kBlkRows : rpw);
@@ -399,7 +399,7 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
             hipLaunchKernelGGL(softmax_hub_merge_kernel<HH>, dim3(grid_for(plan->hub_capacity, 1, kPersistentBlocks)),
                                dim3(kBlock), 0, stream, *plan);
             hipLaunchKernelGGL(softmax_hub_write_kernel<HH>,
-                               dim3(grid_for(plan->hubseg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0, stream,
+                               dim3(grid_for(plan->hubseg_capacity, 1, kSegmentGrid)), dim3(kBlock), 0, stream,
                                row_ptr, scores, out, *plan);
         }
     });

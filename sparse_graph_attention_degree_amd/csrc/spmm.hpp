@@ -474,9 +474,10 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------------------------
 // Long rows and hub segments: one 256-thread workgroup per segment of the plan's segment table
-// (persistent grid, counts read on the device).  The 4*P slots split the segment's edges into
-// contiguous sub-ranges, leave their states in LDS, and the workgroup merges them.  A long row
-// (slot < 0) is written out; a hub segment's state goes to the plan's partial buffer.
+// (a grid of up to kSegmentGrid workgroups striding over the table; counts read on the device).  The
+// 4*P slots split the segment's edges into contiguous sub-ranges, leave their states in LDS, and
+// the workgroup merges them.  A long row (slot < 0) is written out; a hub segment's state goes to
+// the plan's partial buffer.
 template <typename T, int H, int D, int MODE, class TAB>
 __global__ __launch_bounds__(kBlock) void spmm_segment_kernel(const int32_t* __restrict__ col, int64_t n_src,
                                                               const float* __restrict__ sc,
@@ -657,7 +658,7 @@ hipError_t launch_spmm_mode(int dtype, int H, int D, const int32_t* row_ptr, con
             using TAB = typename decltype(tab_tag)::type;
             if (plan)
                 hipLaunchKernelGGL((spmm_segment_kernel<T, HH, DD, MODE, TAB>),
-                                   dim3(grid_for(plan->seg_capacity, 1, kPersistentBlocks)), dim3(kBlock), 0,
+                                   dim3(grid_for(plan->seg_capacity, 1, kSegmentGrid)), dim3(kBlock), 0,
                                    stream, col, n_src, sc, qt, kt, vt, scale, out, *plan);
             if (small)
                 hipLaunchKernelGGL((spmm_short_kernel<T, HH, DD, MODE, TAB, kShortSlotLanes, 1>), dim3(blocks),
