@@ -62,7 +62,7 @@ typedef enum gat_status {
     GAT_ERR_NULL = 1,         /* a required pointer is NULL */
     GAT_ERR_SIZE = 2,         /* a size is negative or does not fit int32 */
     GAT_ERR_UNSUPPORTED = 3,  /* (heads, head_dim, dtype) outside the supported set */
-    GAT_ERR_WORKSPACE = 4,    /* plan workspace too small, or plan built for other sizes */
+    GAT_ERR_WORKSPACE = 4,    /* plan workspace too small, or plan built for another row_ptr or sizes */
     GAT_ERR_ARGS = 5,         /* inconsistent arguments (e.g. both or neither of scores / q,k) */
     GAT_ERR_HIP = 6           /* a HIP call or kernel launch failed */
 } gat_status;
@@ -83,7 +83,10 @@ typedef enum gat_status {
  *                  hub segment first (slot = its index), then every long row
  *                  (slot = -1), both in increasing row id.
  *   hub table      int32 [hub_capacity][4]: (row, first segment, n segments, 0)
- *   counts         int32 [8]: n_segments, n_hub_segments, n_hubs, n_long_rows
+ *   counts         int32 [8]: n_segments, n_hub_segments, n_hubs, n_long_rows, overflow
+ *                  (overflow = 1: the degrees of row_ptr sum past what n_edges allows, i.e.
+ *                  row_ptr[n_rows] > n_edges; every table is then left empty, nothing is
+ *                  written past the workspace, and rows above short_max get no output)
  *   partials       fp32 [hubseg_capacity][state_floats]: per hub segment
  *                  (max[heads], sum[heads], acc[heads*head_dim])
  */
@@ -96,6 +99,7 @@ typedef struct gat_plan {
     int64_t n_blocks;                /* binner blocks */
     void* ws;
     size_t ws_bytes;
+    const int32_t* row_ptr;          /* the array the plan was built from; calls must pass the same one */
     size_t off_counts, off_blocks, off_segs, off_hubs, off_partials;   /* byte offsets into ws */
     uint32_t magic;
 } gat_plan;

@@ -115,9 +115,12 @@ gat::PlanView plan_view(const gat_plan* p) {
     return v;
 }
 
-// A plan usable for a call on (n_rows, n_edges) needing `floats` floats of state per hub segment.
-gat_status check_plan(const gat_plan* p, int64_t n_rows, int64_t n_edges, int64_t floats) {
+// A plan usable for a call on this row_ptr array and (n_rows, n_edges), needing `floats` floats of
+// state per hub segment.  A plan built from another array (even one of the same sizes) would
+// leave the rows it does not cover unwritten, so it is refused.
+gat_status check_plan(const gat_plan* p, const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, int64_t floats) {
     if (p->magic != kPlanMagic || p->ws == nullptr) return GAT_ERR_ARGS;
+    if (p->row_ptr != row_ptr) return GAT_ERR_WORKSPACE;
     if (p->n_rows != n_rows || p->n_edges != n_edges) return GAT_ERR_WORKSPACE;
     if (floats > p->state_floats) return GAT_ERR_WORKSPACE;
     return GAT_OK;
@@ -143,6 +146,7 @@ hipError_t build_plan(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, i
     p->n_blocks = L.n_blocks;
     p->ws = ws;
     p->ws_bytes = ws_bytes;
+    p->row_ptr = row_ptr;
     p->off_counts = L.off_counts;
     p->off_blocks = L.off_blocks;
     p->off_segs = L.off_segs;
@@ -153,7 +157,7 @@ hipError_t build_plan(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, i
     return gat::launch_plan(row_ptr, n_rows, short_max, seg_len, reinterpret_cast<int4*>(base + L.off_blocks),
                             L.n_blocks, reinterpret_cast<int32_t*>(base + L.off_counts),
                             reinterpret_cast<int4*>(base + L.off_segs), reinterpret_cast<int4*>(base + L.off_hubs),
-                            stream);
+                            gat::PlanCaps{L.seg_cap, L.hub_cap, L.hubseg_cap}, stream);
 }
 
 // ------------------------------------------------------------------------------ transposed view
@@ -293,7 +297,7 @@ gat_status gat_edge_softmax(const int32_t* row_ptr, int64_t n_rows, int64_t n_ed
     if (!row_ptr || !scores || !out) return GAT_ERR_NULL;
     gat::PlanView pv;
     if (plan) {
-        const gat_status st = check_plan(plan, n_rows, n_edges, 2 * (int64_t)heads);
+        const gat_status st = check_plan(plan, row_ptr, n_rows, n_edges, 2 * (int64_t)heads);
         if (st != GAT_OK) return st;
         pv = plan_view(plan);
     }
@@ -311,7 +315,7 @@ gat_status gat_aggregate(const int32_t* row_ptr, const int32_t* col_idx, int64_t
     if (n_edges > 0 && n_src == 0) return GAT_ERR_ARGS;
     gat::PlanView pv;
     if (plan) {
-        const gat_status st = check_plan(plan, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
+        const gat_status st = check_plan(plan, row_ptr, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
         if (st != GAT_OK) return st;
         pv = plan_view(plan);
     }
@@ -319,23 +323,40 @@ gat_status gat_aggregate(const int32_t* row_ptr, const int32_t* col_idx, int64_t
                                        nullptr, nullptr, feat, 1.f, out, plan ? &pv : nullptr, stream));
 }
 
-gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
-                           int64_t n_edges, int heads, int head_dim, gat_dtype dtype, const float* scores,
-                           const void* q, const void* k, float scale, const void* v, float* out,
-                           const gat_plan* plan, hipStream_t stream) {
+// Argument checks of gat_fused_layer and its allocation-free variant (everything but the plan).
+// GAT_OK with *nothing = true: no rows, nothing to enqueue.
+gat_status check_fused(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                       int64_t n_edges, int heads, int head_dim, gat_dtype dtype, const float* scores, const void* q,
+                       const void* k, const void* v, const float* out, bool* nothing) {
+    *nothing = false;
     if (!size_ok(n_rows) || !size_ok(n_src) || !edges_ok(n_edges)) return GAT_ERR_SIZE;
     if (!shape_ok(heads, head_dim) || !dtype_ok(dtype)) return GAT_ERR_UNSUPPORTED;
     const bool have_scores = scores != nullptr;
     const bool have_q = q != nullptr, have_k = k != nullptr;
     // With no edges the output is +0.0 whatever the mode, and empty tensors carry NULL data pointers.
     if (n_edges > 0 && (have_q != have_k || have_scores == have_q)) return GAT_ERR_ARGS;
-    if (n_rows == 0) return GAT_OK;
+    if (n_rows == 0) {
+        *nothing = true;
+        return GAT_OK;
+    }
     if (!row_ptr || !out) return GAT_ERR_NULL;
     if (n_edges > 0 && (!col_idx || !v)) return GAT_ERR_NULL;
     if (n_edges > 0 && n_src == 0) return GAT_ERR_ARGS;
+    return GAT_OK;
+}
+
+gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                           int64_t n_edges, int heads, int head_dim, gat_dtype dtype, const float* scores,
+                           const void* q, const void* k, float scale, const void* v, float* out,
+                           const gat_plan* plan, hipStream_t stream) {
+    bool nothing = false;
+    const gat_status chk = check_fused(row_ptr, col_idx, n_rows, n_src, n_edges, heads, head_dim, dtype, scores, q,
+                                       k, v, out, &nothing);
+    if (chk != GAT_OK || nothing) return chk;
+    const bool have_scores = scores != nullptr;
     gat::PlanView pv;
     if (plan) {
-        const gat_status st = check_plan(plan, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
+        const gat_status st = check_plan(plan, row_ptr, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
         if (st != GAT_OK) return st;
         pv = plan_view(plan);
     }
@@ -469,7 +490,7 @@ gat_status gat_edge_softmax_backward(const int32_t* row_ptr, int64_t n_rows, int
     if (!row_ptr || !alpha || !grad || !out) return GAT_ERR_NULL;
     gat::PlanView pv;
     if (plan) {
-        const gat_status st = check_plan(plan, n_rows, n_edges, heads);
+        const gat_status st = check_plan(plan, row_ptr, n_rows, n_edges, heads);
         if (st != GAT_OK) return st;
         pv = plan_view(plan);
     }
@@ -523,7 +544,7 @@ gat_status gat_fused_layer_backward(const int32_t* row_ptr, const int32_t* col_i
     if (n_edges > 0 && (have_q != have_k || have_scores == have_q)) return GAT_ERR_ARGS;
     const bool layer = !have_scores && have_q;
     if (plan == nullptr || csc == nullptr || ws == nullptr) return GAT_ERR_NULL;
-    gat_status st = check_plan(plan, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
+    gat_status st = check_plan(plan, row_ptr, n_rows, n_edges, (int64_t)heads * (head_dim + 2));
     if (st != GAT_OK) return st;
     st = check_csc(csc, n_rows, n_src, n_edges, heads, head_dim);
     if (st != GAT_OK) return st;

@@ -83,9 +83,11 @@ __global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* __res
     if (threadIdx.x == 0) blocks[blockIdx.x] = make_int4(tot.a, tot.b, tot.c, 0);
 }
 
-// One workgroup: exclusive scan of the per-block counts (in place) and the totals.
+// One workgroup: exclusive scan of the per-block counts (in place) and the totals.  Totals past
+// the table capacities (a row_ptr whose degrees sum past n_edges) set the overflow flag and
+// leave every table empty, so no kernel reads or writes past the workspace.
 __global__ __launch_bounds__(kBlock) void plan_scan_kernel(int4* __restrict__ blocks, int64_t n_blocks,
-                                                           int32_t* __restrict__ counts) {
+                                                           int32_t* __restrict__ counts, PlanCaps caps) {
     Triple carry = {0, 0, 0};
     for (int64_t base = 0; base < n_blocks; base += kBlock) {
         const int64_t i = base + threadIdx.x;
@@ -100,10 +102,13 @@ __global__ __launch_bounds__(kBlock) void plan_scan_kernel(int4* __restrict__ bl
         carry = add(carry, tot);
     }
     if (threadIdx.x == 0) {
-        counts[kNSegs] = carry.c + carry.a;
-        counts[kNHubSegs] = carry.c;
-        counts[kNHubs] = carry.b;
-        counts[kNLong] = carry.a;
+        const bool over = (int64_t)carry.c + carry.a > caps.segs || carry.b > caps.hubs || carry.c > caps.hub_segs ||
+                          carry.a < 0 || carry.b < 0 || carry.c < 0;
+        counts[kNSegs] = over ? 0 : carry.c + carry.a;
+        counts[kNHubSegs] = over ? 0 : carry.c;
+        counts[kNHubs] = over ? 0 : carry.b;
+        counts[kNLong] = over ? 0 : carry.a;
+        counts[kOverflow] = over ? 1 : 0;
     }
 }
 
@@ -129,6 +134,7 @@ __global__ __launch_bounds__(kBlock) void plan_scatter_kernel(const int32_t* __r
     }
     Triple tot;
     const Triple ex = block_exscan(c, tot);
+    if (counts[kOverflow]) return;   // the tables stay empty
     const int4 base = blocks[blockIdx.x];
     const int n_hub_segs = counts[kNHubSegs];
     int pos_long = base.x + ex.a, pos_hub = base.y + ex.b, pos_hs = base.z + ex.c;
@@ -151,11 +157,12 @@ __global__ __launch_bounds__(kBlock) void plan_scatter_kernel(const int32_t* __r
 }  // namespace
 
 hipError_t launch_plan(const int32_t* row_ptr, int64_t n_rows, int short_max, int seg_len, int4* blocks,
-                       int64_t n_blocks, int32_t* counts, int4* segs, int4* hubs, hipStream_t stream) {
+                       int64_t n_blocks, int32_t* counts, int4* segs, int4* hubs, PlanCaps caps,
+                       hipStream_t stream) {
     if (n_blocks > 0)
         hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)n_blocks), dim3(kBlock), 0, stream, row_ptr, n_rows,
                            short_max, seg_len, blocks);
-    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kBlock), 0, stream, blocks, n_blocks, counts);
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kBlock), 0, stream, blocks, n_blocks, counts, caps);
     if (n_blocks > 0)
         hipLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)n_blocks), dim3(kBlock), 0, stream, row_ptr,
                            n_rows, short_max, seg_len, blocks, counts, segs, hubs);

@@ -82,6 +82,17 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Hand-off point between the lanes of one wave through LDS: a value one lane wrote is read by
+// another lane after this point, or an area other lanes read before this point is rewritten
+// after it.  A wave's LDS instructions execute in issue order, so the hardware needs no wait;
+// the two wave-scope fences keep the compiler from moving memory accesses across the point
+// (without them only its failure to prove two lanes' addresses distinct keeps the order).
+__device__ __forceinline__ void wave_lds_handoff() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // e^x as the hardware exp2 of x*log2(e).  exp(-inf) = 0.
 __device__ __forceinline__ float exp_fast(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
@@ -151,7 +162,7 @@ struct Tab64 {
 // ---------------------------------------------------------------------------- plan view
 // Device view of a degree-binning plan (see gat_plan in gat.h).
 struct PlanView {
-    const int32_t* counts;    // [0] n_segments [1] n_hub_segments [2] n_hubs [3] n_long
+    const int32_t* counts;    // [0] n_segments [1] n_hub_segments [2] n_hubs [3] n_long [4] overflow
     const int4* segs;         // (row, e_begin, e_end, slot)
     const int4* hubs;         // (row, first segment, n segments, 0)
     float* partials;          // [hub segment][state_floats]
@@ -176,6 +187,8 @@ constexpr int64_t kSegmentGrid = 65536;
 // workgroups looping over the edges took 7.09 ms against 6.77 ms.
 constexpr int64_t kEdgeGrid = int64_t(1) << 23;
 
-enum CountIdx { kNSegs = 0, kNHubSegs = 1, kNHubs = 2, kNLong = 3 };
+// kOverflow: 1 when the row degrees sum past the capacities the host sized from n_edges (row_ptr
+// breaks its precondition row_ptr[n_rows] = n_edges); the binner then leaves every table empty.
+enum CountIdx { kNSegs = 0, kNHubSegs = 1, kNHubs = 2, kNLong = 3, kOverflow = 4 };
 
 }  // namespace gat

@@ -81,9 +81,14 @@ inline unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
 // Every launcher enqueues on `stream` and returns hipGetLastError() (hipErrorInvalidValue
 // for an unsupported shape, which the C-ABI has already ruled out).
 
+// capacities of the plan's tables (entries)
+struct PlanCaps {
+    int64_t segs, hubs, hub_segs;
+};
+
 hipError_t launch_plan(const int32_t* row_ptr, int64_t n_rows, int short_max, int seg_len,
                        int4* blocks, int64_t n_blocks, int32_t* counts, int4* segs, int4* hubs,
-                       hipStream_t stream);
+                       PlanCaps caps, hipStream_t stream);
 
 hipError_t launch_sddmm(int dtype, int H, int D, const int32_t* src_idx, const int32_t* dst_idx,
                         int64_t n_edges, const void* src_feat, int64_t n_src, const void* dst_feat,

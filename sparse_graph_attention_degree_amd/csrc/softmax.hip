@@ -134,9 +134,11 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         // stage the run (all loads issued before the first LDS write)
         float v[kBlkBudget / kWave];
         load_run(src, len, lane, v);
+        wave_lds_handoff();   // the previous group's stage reads come before this rewrite
 #pragma unroll
         for (int t = 0; t < kBlkBudget / kWave; ++t)
             if (t * kWave < len) stage[t * kWave + lane] = v[t];
+        wave_lds_handoff();   // staged by lane l, read by the lane of each (row, head)
         // one lane per (row, head); the exponentials of the sum pass are kept in the stage and
         // scaled in place
         const int pairs = (j - i) * H;
@@ -162,6 +164,7 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 for (int x = b; x < e; ++x) stage[x * H + h] *= rz;
             }
         }
+        wave_lds_handoff();   // alpha written by the (row, head) lanes, stored by lane l
 #pragma unroll
         for (int t = 0; t < kBlkBudget / kWave; ++t)
             if (t * kWave < len) bstore(dst, stage[t * kWave + lane], (lane + t * kWave) * 4);

@@ -167,14 +167,17 @@ struct Engine {
 #pragma unroll
             for (int k = 0; k < SM; ++k) p[k] = k * SC1 + es < n ? s[k] : 0.f;
         }
-        // weights transposed to [head][edge] and column ids into the slot's LDS area; LDS
-        // operations of one wave run in order, so the reads below see these writes.  Staged
-        // before the next chunk's loads are issued, so waiting for (s, cv) never waits on them.
+        // weights transposed to [head][edge] and column ids into the slot's LDS area, which the
+        // slot's lanes read back below (and read for the previous chunk before this rewrite).
+        // Staged before the next chunk's loads are issued, so waiting for (s, cv) never waits
+        // on them.
+        wave_lds_handoff();
 #pragma unroll
         for (int k = 0; k < SM; ++k) stage[(q % H) * SC + k * SC1 + es] = p[k];
 #pragma unroll
         for (int k = 0; k < CM; ++k)
             if (k * G + q < SC) reinterpret_cast<int*>(stage)[H * SC + k * G + q] = cv[k];
+        wave_lds_handoff();
         if (nc < ne) load_chunk(col, sc, nc, ne, s_n, cv_n);
 #pragma unroll
         for (int jb = 0; jb < SC; jb += U) {
@@ -212,9 +215,12 @@ struct Engine {
                                                   float scale, int c, int e1, const int (&cv)[CM], int nc, int ne,
                                                   int (&cv_n)[CM], const T* __restrict__ qn, uint4 (&qraw_n)[NV]) {
         const int n = (e1 - c) < SC ? (e1 - c) : SC;
+        // column ids into the slot's LDS area for every lane of the slot (see consume_scores)
+        wave_lds_handoff();
 #pragma unroll
         for (int k = 0; k < CM; ++k)
             if (k * G + q < SC) reinterpret_cast<int*>(stage)[H * SC + k * G + q] = cv[k];
+        wave_lds_handoff();
         if (nc < ne) {
             float unused[SM];
             load_chunk(col, nullptr, nc, ne, unused, cv_n);
@@ -354,7 +360,7 @@ struct Engine {
             float s_n[SM] = {};
             int cv_n[CM] = {};
             if constexpr (MODE == kLayer) {
-                uint4 unused[NV];
+                uint4 unused[NV] = {};
                 consume_layer(col, kt, vt, scale, c, e, cv, c + SC, e, cv_n, nullptr, unused);
             } else {
                 consume_scores(col, sc, vt, c, e, s, cv, c + SC, e, s_n, cv_n);
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
         }
         float s_n[SM] = {};
         int cv_n[CM] = {};
-        uint4 qraw_n[NV];
+        uint4 qraw_n[NV] = {};   // the next row's query (kLayer): loaded whenever it is used
         if constexpr (MODE == kLayer) {
             const T* qn = (nit != it && nit < RS) ? qf + (row0 + nit) * HD : nullptr;
             eng.consume_layer(col, kt, vt, scale, c, e1, cv, nc, ne, cv_n, qn, qraw_n);

@@ -44,7 +44,7 @@ class GatPlanStruct(ctypes.Structure):
                 ("state_floats", ctypes.c_int64),
                 ("seg_capacity", ctypes.c_int64), ("hub_capacity", ctypes.c_int64),
                 ("hubseg_capacity", ctypes.c_int64), ("n_blocks", ctypes.c_int64),
-                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("row_ptr", ctypes.c_void_p),
                 ("off_counts", ctypes.c_size_t), ("off_blocks", ctypes.c_size_t), ("off_segs", ctypes.c_size_t),
                 ("off_hubs", ctypes.c_size_t), ("off_partials", ctypes.c_size_t),
                 ("magic", ctypes.c_uint32)]

@@ -56,7 +56,7 @@ def test_plan_struct_layout(L):
 
 def test_status_strings(L):
     for s in range(7):
-        assert L.gat_status_str(s)
+        assert L.gat_status_str(s) and L.gat_status_str(s) != b"unknown status"
     assert L.gat_status_str(99) == b"unknown status"
 
 
@@ -125,6 +125,20 @@ def test_fused_layer_host_checks(L):
     assert f(FAKE, FAKE, 4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, None, FAKE, None, None) == NULL   # v missing
     assert f(FAKE, FAKE, 4, 4, 5, 5, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None, None) == UNSUP
     assert f(FAKE, FAKE, -4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None, None) == SIZE
+
+
+def test_plan_refused_for_another_row_ptr(L):
+    """A plan is tied to the row_ptr array it was built from: a call with another array of the same
+    sizes is refused on the host (it would leave the rows the plan does not cover unwritten)."""
+    p = gat.GatPlanStruct()
+    p.magic, p.ws, p.n_rows, p.n_edges = 0x47415450, 0x2000, 4, 5
+    p.state_floats, p.row_ptr = 4 * 66, 0x3000
+    other = ctypes.c_void_p(0x4000)
+    assert L.gat_edge_softmax(other, 4, 5, 1, FAKE, FAKE, ctypes.byref(p), None) == WS
+    assert L.gat_aggregate(other, FAKE, 4, 4, 5, FAKE, FAKE, 0, 1, 64, FAKE, ctypes.byref(p), None) == WS
+    assert L.gat_fused_layer(other, FAKE, 4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE,
+                             ctypes.byref(p), None) == WS
+    assert L.gat_edge_softmax_backward(other, 4, 5, 1, FAKE, FAKE, FAKE, ctypes.byref(p), None) == WS
 
 
 def test_plan_build_host_checks(L):

@@ -50,10 +50,28 @@ def test_plan_tables_bit_exact(sched):
     counts = to_np(plan.table("counts"))
     assert counts[0] == len(segs) and counts[1] == nhs and counts[2] == len(hubs)
     assert counts[3] == len(segs) - nhs
+    assert counts[4] == 0   # no overflow
     got_segs = to_np(plan.table("segs")).reshape(-1, 4)[: len(segs)]
     got_hubs = to_np(plan.table("hubs")).reshape(-1, 4)[: len(hubs), :3]
     assert np.array_equal(got_segs, segs)
     assert np.array_equal(got_hubs, hubs)
+
+
+def test_plan_overflow_flag():
+    """A row_ptr whose degrees sum far past the n_edges the plan was sized for (a broken
+    precondition): the binner flags it, leaves every table empty and writes nothing past its
+    workspace.  Only the binner runs here; it reads row_ptr alone."""
+    g = mixed_graph(5)
+    rp = to_dev(g.row_ptr)
+    ws_need = gat.gat_plan_workspace_bytes(g.n_rows, 100, 4, 64)
+    ws = torch.zeros(ws_need + 4096, dtype=torch.uint8, device=rp.device)
+    ws[ws_need:] = 0xA5   # guard band past the workspace the plan may use
+    plan = gat.gat_plan_build(rp, 100, 4, 64, ws=ws[:ws_need])
+    counts = to_np(plan.table("counts"))
+    assert counts[4] == 1 and np.all(counts[:4] == 0)
+    assert np.all(to_np(ws[ws_need:]) == 0xA5)
+    good = to_np(gat.gat_plan_build(rp, g.n_edges, 4, 64).table("counts"))
+    assert good[4] == 0 and good[0] > 0
 
 
 def test_plan_tables_c5_bit_exact():
