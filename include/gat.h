@@ -20,7 +20,8 @@
  * ---------------------------------------
  *  - Pointers are DEVICE pointers (memory of the current HIP device) unless the
  *    comment says host.  The caller owns every buffer; the library allocates and
- *    frees nothing and keeps no state between calls.
+ *    frees nothing and keeps no state between calls (the one exception,
+ *    gat_fused_layer_noalloc, keeps its plan in a device array of its own).
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *    without waiting.  No entry point synchronises.
  *  - Layouts (row-major, contiguous):
@@ -64,7 +65,8 @@ typedef enum gat_status {
     GAT_ERR_UNSUPPORTED = 3,  /* (heads, head_dim, dtype) outside the supported set */
     GAT_ERR_WORKSPACE = 4,    /* plan workspace too small, or plan built for another row_ptr or sizes */
     GAT_ERR_ARGS = 5,         /* inconsistent arguments (e.g. both or neither of scores / q,k) */
-    GAT_ERR_HIP = 6           /* a HIP call or kernel launch failed */
+    GAT_ERR_HIP = 6,          /* a HIP call or kernel launch failed */
+    GAT_ERR_SCRATCH = 7       /* the graph's plan exceeds the library's fixed scratch array */
 } gat_status;
 
 /* Degree-binning defaults: rows with deg <= short_max are handled by one lane group
@@ -174,6 +176,36 @@ gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64
                            int64_t n_edges, int heads, int head_dim, gat_dtype dtype,
                            const float* scores, const void* q, const void* k, float scale,
                            const void* v, float* out, const gat_plan* plan, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gat_fused_layer with a degree-binning plan (default
+ * thresholds) that the call builds itself, on `stream`, in a device array the library owns,
+ * instead of a caller workspace.  Same arguments, modes, layouts and results as
+ * gat_fused_layer given a plan from gat_plan_build with the default thresholds (the same
+ * kernels on the same tables, so the outputs are bitwise equal).
+ *  - The array is GAT_NOALLOC_SCRATCH_BYTES per GPU, a file-scope device array: each GPU the
+ *    library runs this call on holds it from that call until the process ends.  The call
+ *    itself allocates and frees nothing.  Its first call on a device looks the array up
+ *    (hipGetSymbolAddress) and loads the library's code object there if needed, so make one
+ *    call before capturing a graph.
+ *  - A graph whose plan needs more than the array (gat_fused_layer_noalloc_bytes > the
+ *    maximum: e.g. 2^20 rows and 2^24 edges at 4 x 64 need 39 MB and fit; 2^22 rows and
+ *    2^26 edges at 8 x 16 need 94 MB and do not) returns GAT_ERR_SCRATCH and enqueues nothing.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last call's plan.
+ *    Calls that overlap on one GPU (on different streams, or from several host threads
+ *    without ordering) race on it and give wrong results; calls ordered on one stream are
+ *    safe.  Nothing in the array has to start at zero.
+ */
+#define GAT_NOALLOC_SCRATCH_BYTES (64u << 20)
+gat_status gat_fused_layer_noalloc(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows,
+                                   int64_t n_src, int64_t n_edges, int heads, int head_dim,
+                                   gat_dtype dtype, const float* scores, const void* q, const void* k,
+                                   float scale, const void* v, float* out, hipStream_t stream);
+
+/* Bytes of the library's scratch array that gat_fused_layer_noalloc needs for these sizes
+ * (0 for invalid sizes); calls above GAT_NOALLOC_SCRATCH_BYTES are refused.  Host only. */
+size_t gat_fused_layer_noalloc_bytes(int64_t n_rows, int64_t n_edges, int heads, int head_dim);
 
 /* Static description of a status code (host; never NULL). */
 const char* gat_status_str(gat_status status);

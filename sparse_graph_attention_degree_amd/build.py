@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "binner.hip", "sddmm.hip", "softmax.hip", "spmm_agg.hip", "spmm_softagg.hip",
            "spmm_layer.hip", "backward.hip", "batch.hip", "relation_block.hip",
-           "linear.hip"]
+           "linear.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -244,6 +244,7 @@ const char* gat_status_str(gat_status s) {
         case GAT_ERR_WORKSPACE: return "plan workspace too small or built for other sizes";
         case GAT_ERR_ARGS: return "inconsistent arguments";
         case GAT_ERR_HIP: return "HIP launch or runtime error";
+        case GAT_ERR_SCRATCH: return "graph too large for the library's fixed scratch array (GAT_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -363,6 +364,35 @@ gat_status gat_fused_layer(const int32_t* row_ptr, const int32_t* col_idx, int64
     const int mode = have_scores ? gat::kSoftAgg : gat::kLayer;
     return hip_status(gat::launch_spmm(mode, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, scores, q, k, v,
                                        scale, out, plan ? &pv : nullptr, stream));
+}
+
+size_t gat_fused_layer_noalloc_bytes(int64_t n_rows, int64_t n_edges, int heads, int head_dim) {
+    if (!size_ok(n_rows) || !edges_ok(n_edges) || !shape_ok(heads, head_dim)) return 0;
+    return plan_layout(n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN).total;
+}
+
+gat_status gat_fused_layer_noalloc(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_src,
+                                   int64_t n_edges, int heads, int head_dim, gat_dtype dtype, const float* scores,
+                                   const void* q, const void* k, float scale, const void* v, float* out,
+                                   hipStream_t stream) {
+    bool nothing = false;
+    const gat_status chk = check_fused(row_ptr, col_idx, n_rows, n_src, n_edges, heads, head_dim, dtype, scores, q,
+                                       k, v, out, &nothing);
+    if (chk != GAT_OK || nothing) return chk;
+    const Layout L = plan_layout(n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN);
+    if (L.total > (size_t)GAT_NOALLOC_SCRATCH_BYTES) return GAT_ERR_SCRATCH;
+    void* ws = nullptr;   // the library's scratch array on this device
+    if (gat::noalloc_scratch(&ws) != hipSuccess) return GAT_ERR_HIP;
+    // Nothing in the plan's area must start at zero: the binner writes the counts, tables and
+    // per-block sums it reads, and every hub partial is written before it is merged.
+    gat_plan p;
+    hipError_t e = build_plan(row_ptr, n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN, L,
+                              ws, (size_t)GAT_NOALLOC_SCRATCH_BYTES, &p, stream);
+    if (e != hipSuccess) return GAT_ERR_HIP;
+    const gat::PlanView pv = plan_view(&p);
+    const int mode = scores != nullptr ? gat::kSoftAgg : gat::kLayer;
+    return hip_status(gat::launch_spmm(mode, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, scores, q, k, v,
+                                       scale, out, &pv, stream));
 }
 
 gat_status gat_batch_csr(const int32_t* local_row_ptr, const int32_t* local_col, const int32_t* row_off,

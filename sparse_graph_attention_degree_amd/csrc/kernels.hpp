@@ -148,6 +148,10 @@ hipError_t launch_relation_block(const float* nodes, const float* pair, const fl
                                  const float* wo, const float* w1, const float* b1, const float* w2, const float* b2,
                                  int64_t B, int N, int D, int H, int P, float* out, hipStream_t stream);
 
+// Device address of the library's own scratch array on the current device (looked up on the
+// first call per device), for the entry point that allocates nothing.
+hipError_t noalloc_scratch(void** addr);
+
 // Rows per binner block (256 threads x 4 consecutive rows).
 constexpr int kPlanRowsPerThread = 4;
 constexpr int kPlanRowsPerBlock = kBlock * kPlanRowsPerThread;

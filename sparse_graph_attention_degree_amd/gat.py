@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libgat.so")
 
 GAT_F32, GAT_BF16 = 0, 1
 STATUS = {0: "GAT_OK", 1: "GAT_ERR_NULL", 2: "GAT_ERR_SIZE", 3: "GAT_ERR_UNSUPPORTED", 4: "GAT_ERR_WORKSPACE",
-          5: "GAT_ERR_ARGS", 6: "GAT_ERR_HIP"}
+          5: "GAT_ERR_ARGS", 6: "GAT_ERR_HIP", 7: "GAT_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DEFAULT_SHORT_MAX = 64
 DEFAULT_SEG_LEN = 1024
 
@@ -27,7 +28,8 @@ EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge
             "gat_fused_layer", "gat_status_str", "gat_shape_supported", "gat_plan_sizeof",
             "gat_csc_workspace_bytes", "gat_csc_sizeof", "gat_csc_build", "gat_edge_softmax_backward",
             "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward",
-            "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block", "gat_linear"]
+            "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block", "gat_linear",
+            "gat_fused_layer_noalloc", "gat_fused_layer_noalloc_bytes"]
 
 
 class GatError(RuntimeError):
@@ -78,6 +80,9 @@ def _lib():
     L.gat_edge_softmax.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     L.gat_aggregate.argtypes = [vp, vp, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp]
     L.gat_fused_layer.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, vp]
+    L.gat_fused_layer_noalloc.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp]
+    L.gat_fused_layer_noalloc_bytes.argtypes = [i64, i64, i32, i32]
+    L.gat_fused_layer_noalloc_bytes.restype = sz
     L.gat_csc_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.gat_csc_workspace_bytes.restype = sz
     L.gat_csc_sizeof.restype = sz
@@ -94,6 +99,7 @@ def _lib():
     L.gat_relation_block.argtypes = [vp, vp, vp, vp, vp, f32] + [vp] * 8 + [i64, i32, i32, i32, i32, vp, vp]
     L.gat_linear.argtypes = [vp, i32, vp, vp, i64, i32, i32, ctypes.POINTER(vp), i32, i32, vp]
     for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer,
+              L.gat_fused_layer_noalloc,
               L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward,
               L.gat_batch_csr, L.gat_relation_block, L.gat_linear):
         f.restype = i32
@@ -267,6 +273,29 @@ def gat_fused_layer(row_ptr, col_idx, v, scores=None, q=None, k=None, scale: flo
                                                      col_idx.numel(), H, D, _feat_dtype(v), _ptr(scores), _ptr(q),
                                                      _ptr(k), float(scale), _ptr(v), _ptr(out),
                                                      plan.ref() if plan else None, _stream(stream)))
+    return out
+
+
+def gat_fused_layer_noalloc_bytes(n_rows, n_edges, heads, head_dim) -> int:
+    return int(_lib().gat_fused_layer_noalloc_bytes(n_rows, n_edges, heads, head_dim))
+
+
+def gat_fused_layer_noalloc(row_ptr, col_idx, v, out, scores=None, q=None, k=None, scale: float = 1.0, stream=None):
+    """gat_fused_layer with the degree-binning plan built inside the library's own device array
+    (no workspace, no allocation by the library); ``out`` (fp32 [N,H,D]) must be given."""
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(col_idx, "col_idx", torch.int32, 1)
+    _dev(v, "v", None, 3)
+    _dev(scores, "scores", torch.float32, 2)
+    _dev(q, "q", v.dtype, 3)
+    _dev(k, "k", v.dtype, 3)
+    _dev(out, "out", torch.float32, 3)
+    n_rows = row_ptr.numel() - 1
+    H, D = v.shape[1:]
+    _check("gat_fused_layer_noalloc",
+           _lib().gat_fused_layer_noalloc(_ptr(row_ptr), _ptr(col_idx), n_rows, v.shape[0], col_idx.numel(), H, D,
+                                          _feat_dtype(v), _ptr(scores), _ptr(q), _ptr(k), float(scale), _ptr(v),
+                                          _ptr(out), _stream(stream)))
     return out
 
 

@@ -17,7 +17,7 @@ import oracle.binning as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gat.h")
 
-OK, NULL, SIZE, UNSUP, WS, ARGS = 0, 1, 2, 3, 4, 5
+OK, NULL, SIZE, UNSUP, WS, ARGS, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @pytest.fixture(scope="module")
@@ -55,7 +55,7 @@ def test_plan_struct_layout(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert L.gat_status_str(s) and L.gat_status_str(s) != b"unknown status"
     assert L.gat_status_str(99) == b"unknown status"
 
@@ -125,6 +125,30 @@ def test_fused_layer_host_checks(L):
     assert f(FAKE, FAKE, 4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, None, FAKE, None, None) == NULL   # v missing
     assert f(FAKE, FAKE, 4, 4, 5, 5, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None, None) == UNSUP
     assert f(FAKE, FAKE, -4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None, None) == SIZE
+
+
+def test_noalloc_host_checks(L):
+    """The allocation-free fused layer: the same argument checks as gat_fused_layer, and a graph
+    whose plan exceeds the library's fixed array is refused before anything is enqueued."""
+    f = L.gat_fused_layer_noalloc
+    args = lambda sc, q, k: (FAKE, FAKE, 4, 4, 5, 4, 64, 0, sc, q, k, 1.0, FAKE, FAKE, None)  # noqa: E731
+    assert f(*args(FAKE, FAKE, FAKE)) == ARGS
+    assert f(*args(None, None, None)) == ARGS
+    assert f(*args(None, FAKE, None)) == ARGS
+    assert f(FAKE, FAKE, 4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, None, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 4, 4, 5, 5, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, FAKE, -4, 4, 5, 4, 64, 0, FAKE, None, None, 1.0, FAKE, FAKE, None) == SIZE
+    assert f(None, None, 0, 0, 0, 4, 64, 0, None, None, None, 1.0, None, None, None) == OK
+    # 2^22 rows, 2^26 edges, 8 x 16: the plan needs ~94 MB, the array holds 64 MiB
+    need = L.gat_fused_layer_noalloc_bytes(2**22, 2**26, 8, 16)
+    assert need > gat.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, FAKE, 2**22, 2**22, 2**26, 8, 16, 0, FAKE, None, None, 1.0, FAKE, FAKE, None) == SCRATCH
+    # the metric workload (2^20 rows, 2^24 edges, 4 x 64) fits, and the sizes are the planned call's
+    need4 = L.gat_fused_layer_noalloc_bytes(2**20, 2**24, 4, 64)
+    assert 0 < need4 <= gat.NOALLOC_SCRATCH_BYTES
+    assert need4 == L.gat_plan_workspace_bytes(2**20, 2**24, 4, 64, -1, 0)
+    assert L.gat_fused_layer_noalloc_bytes(-1, 5, 4, 64) == 0
+    assert L.gat_fused_layer_noalloc_bytes(4, 5, 3, 64) == 0
 
 
 def test_plan_refused_for_another_row_ptr(L):
