@@ -27,6 +27,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c5|c3|
                        [--backward]
        python bench.py --workload relation|projection   # the dense l2_p4 block / the projections
        python bench.py --mode copy      # plain-copy calibration target for the counters
+       python bench.py --mode gather    # gather calibration target (every table row read once)
 """
 from __future__ import annotations
 
@@ -93,6 +94,30 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     torch.cuda.synchronize()
     print(json.dumps({"mode": "copy", "bytes_read_per_call": nbytes, "bytes_written_per_call": nbytes,
                       "calls": reps}))
+
+
+def gather_calibration(n=1 << 20, heads=4, head_dim=64, reps=3):
+    """Counter calibration target with a known gather footprint: the aggregation kernel on a
+    graph of n rows with one edge each, whose columns are a permutation of the n sources, so
+    every row of the bf16 [n, heads, head_dim] table (512 MB at the defaults, twice the Infinity
+    Cache) is gathered exactly once.  Prints the bytes every call must read and write."""
+    import torch
+    from sparse_graph_attention_degree_amd import gat
+    dev = torch.device("cuda:0")
+    r = np.random.default_rng(5)
+    rp = torch.arange(n + 1, dtype=torch.int32, device=dev)
+    col = torch.from_numpy(r.permutation(n).astype(np.int32)).to(dev)
+    wts = torch.ones((n, heads), dtype=torch.float32, device=dev)
+    x = torch.randn((n, heads, head_dim), dtype=torch.float32, device=dev).to(torch.bfloat16)
+    out = torch.empty((n, heads, head_dim), dtype=torch.float32, device=dev)
+    for _ in range(reps):
+        gat.gat_aggregate(rp, col, wts, x, out=out)
+    torch.cuda.synchronize()
+    rows = n * heads * head_dim * 2
+    print(json.dumps({"mode": "gather", "kernel": "spmm_short_kernel (aggregate, no plan)", "calls": reps,
+                      "gathered_row_bytes_per_call": rows,
+                      "bytes_read_per_call": 4 * (n + 1) + 4 * n + 4 * n * heads + rows,
+                      "bytes_written_per_call": 4 * n * heads * head_dim}))
 
 
 def cpu_baseline(g, w, q, k, v, budget_s=12.0, one_thread_s=4.0):
@@ -421,7 +446,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "relation", "projection"])
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "gather"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--seed", type=int, default=0)
@@ -448,6 +473,9 @@ def main():
     if not os.path.exists(gat.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
+    if args.mode == "gather":
+        gather_calibration()
+        return
 
     if args.workload == "relation":
         bench_relation(args, gat, G)
@@ -545,10 +573,15 @@ def main():
              "fused_alg_bytes": alg,
              "fused_unique_bytes": unique,
              "fused_unique_gbs": unique / t_fused / 1e9,
-             "sddmm_alg_bytes": 8 * E + 2 * E * H * D * feat_bytes + 4 * E * H,
-             "sddmm_gbs": (8 * E + 2 * E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
-             # the destination rows repeat along each CSR row and stay in cache: gathered k rows only
-             "sddmm_k_gather_gbs": (8 * E + E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
+             # the same call priced on unique bytes (every distinct source row read once): a
+             # schedule that reused every gathered row from cache would reach this fraction
+             "fused_unique_frac": unique / t_fused / 1e9 / HBM_PEAK_GBS,
+             # The SDDMM reads two rows per edge, but the destination (query) row repeats along each
+             # CSR row and stays in cache, so only the k gathers reach memory: that count is its
+             # HBM rate; the two-rows-per-edge count is an effective rate, above the HBM peak here.
+             "sddmm_hbm_bytes": 8 * E + E * H * D * feat_bytes + 4 * E * H,
+             "sddmm_hbm_gbs": (8 * E + E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
+             "sddmm_effective_two_row_gbs": (8 * E + 2 * E * H * D * feat_bytes + 4 * E * H) / t_sddmm / 1e9,
              "kernel_source_sha256": kernel_source_digest()}
     if batch_build_ms is not None:
         extra["batch_graphs"] = B
@@ -627,14 +660,19 @@ def main():
     rec = {
         "metric": METRIC, "value": value, "unit": "edge-heads/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.description if B == 1 else f"{B} graphs of: {w.description}", "n_rows": N,
-                   "n_edges": E, "heads": H, "head_dim": D, "features": w.dtype, "seed": args.seed, "batch": B,
+                   "n_edges": E, "heads": H, "head_dim": D, "features": w.dtype, "accumulate": "f32",
+                   "seed": args.seed, "batch": B,
                    "step": "plan (degree binning) + sddmm q.k + fused softmax/aggregate of v"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "fused softmax+aggregate (gat_fused_layer with scores: segment, short-row and "
-                               "hub-merge kernels)"},
+                               "hub-merge kernels)",
+                     "bytes": "algorithmic: row_ptr, col_idx, scores, one gathered source row per edge, the "
+                              "fp32 output; these are bytes past the L2 (the Infinity Cache serves part of "
+                              "them), not bytes on the HBM bus; extra.fused_unique_frac prices the same call "
+                              "on each distinct row read once"},
         "cpu_baseline": cpu,
         "extra": extra,
     }
