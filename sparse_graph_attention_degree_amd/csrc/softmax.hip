@@ -6,21 +6,20 @@
 // slice with stride H, or one block per node with shared-memory reductions.
 // Here, by degree:
 //  * short rows (the common case): a wave takes 32 consecutive rows; their scores
-//    form one contiguous run, which the wave stages into LDS with coalesced loads
-//    (up to kBlkBudget floats at a time, whole rows).  One lane per (row, head)
-//    then computes max, sum of exp and alpha from LDS, and the wave streams alpha
-//    back with coalesced stores: one HBM round trip per group of rows.
+//    form one contiguous run, read in groups of whole rows (up to kBlkBudget floats,
+//    16 consecutive per lane); per (row, head) maxima and sums combine through LDS
+//    atomics that are exact in any order; one HBM round trip per group of rows.
 //  * rows too long for the stage but not binned long (no plan, or a large
 //    short_max): a 32-lane slot per row reads the row 32 values at a time (lane q:
 //    edge q/H, head q%H), per-head max / sum are xor-shuffle trees over lanes q,
 //    q^H, q^2H, ...; three passes: max, sum of exp, write.
 //  * long rows and hub segments (the plan's segment table): a wave per segment,
 //    streaming it in 1024-float chunks with a running (max, sum) per head; a row of
-//    one chunk is written from registers.  Hub rows: their segments' (max, sum)
-//    states merge, then a workgroup per segment writes alpha.
-// Each (row, head) is reduced in an order fixed by the row alone, so a row's
-// result does not depend on the rows around it (a batch of graphs gives every
-// graph's rows the same bits as the graph alone).
+//    one chunk is written from registers.  Hub rows: a workgroup per hub segment
+//    merges the row's segment (max, sum) states and writes alpha.
+// A row's result does not depend on the rows around it (a batch of graphs gives
+// every graph's rows the same bits as the graph alone): each (row, head) is
+// reduced in an order fixed by the row, or with operations exact in any order.
 #include <math.h>
 
 #include "kernels.hpp"
@@ -90,18 +89,51 @@ __global__ __launch_bounds__(kBlock) void softmax_short_kernel(const int32_t* __
 
 constexpr int kBlkRows = 32;       // rows per wave (at most: fewer on graphs too small to fill the device)
 constexpr int64_t kSmFillWaves = 2048;
-constexpr int kBlkBudget = 1024;   // floats staged per wave (4 KB: 16 KB per workgroup, so LDS admits 10)
+constexpr int kBlkBudget = 1024;   // floats per group (whole rows), 16 per lane
 
-// Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per 32 consecutive rows, groups of
-// consecutive such rows staged in LDS.  A row of another class (non-empty, deg > hi) ends a
-// group, since its scores sit between the groups' runs.
+// Per-(row, head) maxima of a group combine with LDS atomic integer max on an order-preserving key
+// of the float (finite scores; -inf maps below every finite value).
+__device__ __forceinline__ int max_key(float x) {
+    const int b = __float_as_int(x);
+    return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float key_max(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+
+// Sums of exp(s - max) combine in 64-bit fixed point: each term, in (0, 1], is truncated to a
+// multiple of 2^-31, so the sum is exact integer arithmetic, the same in any order.  A row of
+// n edges sums to at least 2^31 (its maximum contributes exactly 1), and the truncation moves the
+// sum by less than n 2^-31 relative to that.
+constexpr float kFix = 2147483648.f;   // 2^31
+
+// Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per rpw (<= 32) consecutive rows, in
+// groups of consecutive such rows (whole rows, at most kBlkBudget floats).  A row of another class
+// (non-empty, deg > hi) ends a group, since its scores sit between the groups' runs.
+//
+// Lane l takes floats 16l .. 16l+15 of the group's run: 16 / H consecutive edges of all H heads,
+// read with four 16-byte buffer loads straight into registers (a load past the run reads 0 and is
+// masked).  The row of each edge comes from a table of the group's row starts in LDS (the row
+// lanes mark their first edge; a max-scan over the lane's edges and over the lanes spreads the
+// marks).  Then, per (row, head): the lane folds its own edges of one row (a running value that
+// restarts where the row changes), and LDS atomics combine the lanes' parts -- an integer max of
+// order-preserving keys (exact), then the sum of exp(s - max) in 64-bit fixed point (kFix: exact
+// integer adds) -- so a row's result is the same whatever rows share its group or lane.
+// alpha = exp(s - max) * (2^31 / sum) leaves with four 16-byte buffer stores.
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __restrict__ row_ptr, int64_t n_rows,
                                                                const float* sc, float* out, int hi, int rpw) {
-    __shared__ float stage_all[kWavesPerBlock][kBlkBudget];
-    float* stage = stage_all[threadIdx.x / kWave];
+    constexpr int EPL = 16 / H;                // edges per lane
+    constexpr int RIDB = kBlkBudget / H;       // edges per group, at most: bytes of the row table
+    constexpr int NRH = kBlkRows * H;          // (row, head) slots
+    __shared__ __align__(16) unsigned char rid_all[kWavesPerBlock][RIDB];
+    __shared__ __align__(16) int mk_all[kWavesPerBlock][NRH];            // max keys, then 2^31 / sum
+    __shared__ __align__(16) unsigned long long z_all[kWavesPerBlock][NRH];
+    const int wv = threadIdx.x / kWave;
+    unsigned char* rid_t = rid_all[wv];
+    int* mk = mk_all[wv];
+    float* rzs = reinterpret_cast<float*>(mk);
+    unsigned long long* zs = z_all[wv];
     const int lane = lane_id();
-    const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * rpw;
+    const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerBlock + wv) * rpw;
     if (r0 >= n_rows) return;
     const int nr = (int)((n_rows - r0) < rpw ? (n_rows - r0) : rpw);
     int rb = 0, re = 0;
@@ -118,7 +150,7 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         const uint64_t from_i = i < 64 ? (mine >> i) << i : 0ull;
         if (from_i == 0) break;
         i = __builtin_ctzll(from_i);
-        // the group ends at the next breaker row or where the run would overflow the stage
+        // the group ends at the next breaker row or where the run would overflow kBlkBudget
         const uint64_t br = i < 63 ? (breaker >> (i + 1)) << (i + 1) : 0ull;
         const int jb = br ? __builtin_ctzll(br) : nr;
         const int base = shfl(rb, i);
@@ -131,43 +163,119 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         const int64_t run0 = (int64_t)__builtin_amdgcn_readfirstlane(base) * H;
         const __amdgpu_buffer_rsrc_t src = span(sc + run0, (int64_t)len * 4);
         const __amdgpu_buffer_rsrc_t dst = span(out + run0, (int64_t)len * 4);
-        // stage the run (all loads issued before the first LDS write)
-        float v[kBlkBudget / kWave];
-        load_run(src, len, lane, v);
-        wave_lds_handoff();   // the previous group's stage reads come before this rewrite
+        float x[16];
 #pragma unroll
-        for (int t = 0; t < kBlkBudget / kWave; ++t)
-            if (t * kWave < len) stage[t * kWave + lane] = v[t];
-        wave_lds_handoff();   // staged by lane l, read by the lane of each (row, head)
-        // one lane per (row, head); the exponentials of the sum pass are kept in the stage and
-        // scaled in place
-        const int pairs = (j - i) * H;
-        for (int t = 0; t * kWave < pairs; ++t) {
-            const int pp = t * kWave + lane;
-            const bool live = pp < pairs;
-            const int row = i + (live ? pp / H : 0);
-            const int h = pp % H;
-            const int b = shfl(rb, row) - base, e = shfl(re, row) - base;
-            if (live) {
-                float m = -INFINITY;
-#pragma unroll 8
-                for (int x = b; x < e; ++x) m = fmaxf(m, stage[x * H + h]);
-                float z = 0.f;
-#pragma unroll 8
-                for (int x = b; x < e; ++x) {
-                    const float ex = exp_fast(stage[x * H + h] - m);
-                    stage[x * H + h] = ex;
-                    z += ex;
+        for (int q = 0; q < 4; ++q) {
+            const gat_v4i a = __builtin_amdgcn_raw_buffer_load_b128(src, (lane * 16 + q * 4) * 4, 0, 0);
+            x[4 * q] = __int_as_float(a.x);
+            x[4 * q + 1] = __int_as_float(a.y);
+            x[4 * q + 2] = __int_as_float(a.z);
+            x[4 * q + 3] = __int_as_float(a.w);
+        }
+        const int nrows = j - i;
+        wave_lds_handoff();   // the previous group's table reads come before these rewrites
+        // clear the row table; reset the (row, head) slots
+        if (lane * 16 < RIDB) *reinterpret_cast<uint4*>(rid_t + lane * 16) = make_uint4(0, 0, 0, 0);
+        for (int t = lane; t < nrows * H; t += kWave) {
+            mk[t] = max_key(-INFINITY);
+            zs[t] = 0ull;
+        }
+        wave_lds_handoff();
+        if (lane >= i && lane < j && deg > 0) rid_t[rb - base] = (unsigned char)(lane - i + 1);
+        wave_lds_handoff();
+        // rows of this lane's edges: marks max-scanned along the edges, then over the lanes
+        int rid[EPL];
+        {
+            unsigned char bt[EPL];
+            if constexpr (EPL == 16) {
+                const uint4 w = *reinterpret_cast<const uint4*>(rid_t + lane * 16);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int k = 0; k < 16; ++k) bt[k] = (ww[k / 4] >> (8 * (k % 4))) & 0xff;
+            } else if constexpr (EPL == 8) {
+                const uint2 w = *reinterpret_cast<const uint2*>(rid_t + lane * 8);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) bt[k] = ((k < 4 ? w.x : w.y) >> (8 * (k % 4))) & 0xff;
+            } else if constexpr (EPL == 4) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(rid_t + lane * 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) bt[k] = (w >> (8 * k)) & 0xff;
+            } else if constexpr (EPL == 2) {
+                const uint32_t w = *reinterpret_cast<const uint16_t*>(rid_t + lane * 2);
+                bt[0] = w & 0xff;
+                bt[1] = w >> 8;
+            } else {
+                bt[0] = rid_t[lane];
+            }
+            int run = 0;
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                run = bt[k] > run ? bt[k] : run;
+                rid[k] = run;
+            }
+            int incl = run;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o) incl = y > incl ? y : incl;
+            }
+            int excl = __shfl_up(incl, 1);
+            if (lane == 0) excl = 0;
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) rid[k] = (rid[k] > excl ? rid[k] : excl) - 1;
+        }
+        // per (row, head): the lane's own edges of one row folded (a running value that restarts
+        // where the row changes), then an atomic max of the keys at the row's last edge in the lane
+        {
+            float run[H];
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                const bool valid = (lane * 16 + k * H) < len;
+                const bool restart = k == 0 || rid[k] != rid[k - 1];
+                const bool lastk = k == EPL - 1 || rid[k + 1] != rid[k] || (lane * 16 + (k + 1) * H) >= len;
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    const float v = x[k * H + h];
+                    run[h] = restart ? v : fmaxf(run[h], v);
+                    if (valid && lastk) atomicMax(&mk[rid[k] * H + h], max_key(run[h]));
                 }
-                const float rz = 1.f / z;
-#pragma unroll 8
-                for (int x = b; x < e; ++x) stage[x * H + h] *= rz;
             }
         }
-        wave_lds_handoff();   // alpha written by the (row, head) lanes, stored by lane l
+        wave_lds_handoff();
+        // exp(s - max); its fixed-point sum per (row, head), folded the same way, then atomics
+        {
+            unsigned long long run[H];
 #pragma unroll
-        for (int t = 0; t < kBlkBudget / kWave; ++t)
-            if (t * kWave < len) bstore(dst, stage[t * kWave + lane], (lane + t * kWave) * 4);
+            for (int k = 0; k < EPL; ++k) {
+                const bool valid = (lane * 16 + k * H) < len;
+                const bool restart = k == 0 || rid[k] != rid[k - 1];
+                const bool lastk = k == EPL - 1 || rid[k + 1] != rid[k] || (lane * 16 + (k + 1) * H) >= len;
+                const int slot = (valid ? rid[k] : 0) * H;
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    const float p = valid ? exp_fast(x[k * H + h] - key_max(mk[slot + h])) : 0.f;
+                    x[k * H + h] = p;
+                    const unsigned long long f = (unsigned long long)(unsigned)(p * kFix);
+                    run[h] = restart ? f : run[h] + f;
+                    if (valid && lastk) atomicAdd(&zs[rid[k] * H + h], run[h]);
+                }
+            }
+        }
+        wave_lds_handoff();
+        for (int t = lane; t < nrows * H; t += kWave) rzs[t] = kFix / (float)zs[t];
+        wave_lds_handoff();
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            const bool valid = (lane * 16 + k * H) < len;
+#pragma unroll
+            for (int h = 0; h < H; ++h) x[k * H + h] *= rzs[(valid ? rid[k] : 0) * H + h];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const gat_v4i a = {__float_as_int(x[4 * q]), __float_as_int(x[4 * q + 1]), __float_as_int(x[4 * q + 2]),
+                               __float_as_int(x[4 * q + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(a, dst, (lane * 16 + q * 4) * 4, 0, 0);
+        }
         i = j;
     }
 }
@@ -193,8 +301,11 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
     // the wave index as a scalar, so that the segment entry and the buffer descriptors built
     // from it stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    for (int64_t s = (int64_t)blockIdx.x * kWavesPerBlock + wave; s < n_segs; s += n_waves) {
-        const int4 sg = plan.segs[s];
+    // The table is walked from its end: long rows first, then the hub segments from last to
+    // first, so the hub scores read last (hub segment 0 onwards) are the first ones the alpha pass
+    // reads again, while they may still be in the Infinity Cache.
+    for (int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave; w < n_segs; w += n_waves) {
+        const int4 sg = plan.segs[n_segs - 1 - w];
         const int64_t n = (int64_t)(sg.z - sg.y) * H;
         const float* seg = sc + (int64_t)sg.y * H;
         float v[kSegRegs];
@@ -250,102 +361,82 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
     }
 }
 
-// One workgroup per hub row: merge its segments' (max, sum) states -- the 256 threads split
-// the segments, then an xor-shuffle tree and a 4-wave merge -- and store the merged state in
-// the slot of the row's first segment.
-template <int H>
-__global__ __launch_bounds__(kBlock) void softmax_hub_merge_kernel(PlanView plan) {
-    __shared__ float lm[kWavesPerBlock][H], lz[kWavesPerBlock][H];
-    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
-    const int n_hubs = plan.counts[kNHubs];
-    for (int hb = blockIdx.x; hb < n_hubs; hb += gridDim.x) {
-        const int4 hr = plan.hubs[hb];   // row, first segment, n segments
-        float* p0 = plan.partials + (int64_t)hr.y * plan.state_floats;
-        float m[H], z[H];
-#pragma unroll
-        for (int h = 0; h < H; ++h) {
-            m[h] = -INFINITY;
-            z[h] = 0.f;
-        }
-        for (int c = t; c < hr.z; c += kBlock) {
-            const float* pc = p0 + (int64_t)c * plan.state_floats;
-#pragma unroll
-            for (int h = 0; h < H; ++h) {
-                const float mc = pc[h], zc = pc[H + h];
-                const float mn = fmaxf(m[h], mc);
-                z[h] = (m[h] == -INFINITY ? 0.f : z[h] * exp_fast(m[h] - mn)) +
-                       (mc == -INFINITY ? 0.f : zc * exp_fast(mc - mn));
-                m[h] = mn;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < H; ++h) {
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const float mo = shfl_xor(m[h], o), zo = shfl_xor(z[h], o);
-                const float mn = fmaxf(m[h], mo);
-                z[h] = (m[h] == -INFINITY ? 0.f : z[h] * exp_fast(m[h] - mn)) +
-                       (mo == -INFINITY ? 0.f : zo * exp_fast(mo - mn));
-                m[h] = mn;
-            }
-            if (lane == 0) {
-                lm[w][h] = m[h];
-                lz[w][h] = z[h];
-            }
-        }
-        __syncthreads();
-        if (t < H) {
-            float M = -INFINITY, Z = 0.f;
-#pragma unroll
-            for (int i = 0; i < kWavesPerBlock; ++i) M = fmaxf(M, lm[i][t]);
-#pragma unroll
-            for (int i = 0; i < kWavesPerBlock; ++i)
-                if (lm[i][t] != -INFINITY) Z = fmaf(lz[i][t], exp_fast(lm[i][t] - M), Z);
-            p0[t] = M;
-            p0[H + t] = Z;
-        }
-        __syncthreads();
-    }
-}
-
-// One workgroup per hub segment: read the row's merged state, then write alpha.  The scores of
-// a segment are read in batches, all loads of a batch issued before the first store (out may
-// alias sc, so the compiler would otherwise keep each load-exp-store in order).  The batch loads
-// do not depend on the merged state, so they are issued before it is fetched.  With H >= 4 and
-// 16-byte aligned arrays a segment's run starts on a 16-byte boundary, and threads move 4
-// consecutive floats at a time (heads (4t + j) % H, fixed per thread since 1024 is a multiple
-// of H); otherwise one float at a time.
 constexpr int kHubBatch = 16;   // floats per thread per batch
 
+// (m, z) states merge: m = max(m1, m2), z = z1 e^(m1 - m) + z2 e^(m2 - m); an empty state has
+// m = -inf and contributes nothing.
+__device__ __forceinline__ void merge_state(float& m, float& z, float m2, float z2) {
+    const float mn = fmaxf(m, m2);
+    z = (m == -INFINITY ? 0.f : z * exp_fast(m - mn)) + (m2 == -INFINITY ? 0.f : z2 * exp_fast(m2 - mn));
+    m = mn;
+}
+
+// One workgroup per hub segment.  First the row's merged (max, sum) per head, from its segments'
+// partial states: thread t takes head t % H and segments t / H, t / H + 256 / H, ..., merging them
+// in that order, then block_head_reduce-style trees merge the threads' states (every workgroup
+// of a row computes the same result in the same order).  Then alpha for this segment.  The
+// scores of a segment are read in batches, all loads of a batch issued before the first store
+// (out may alias sc, so the compiler would otherwise keep each load-exp-store in order).  With
+// H >= 4 and 16-byte aligned arrays a segment's run starts on a 16-byte boundary, and threads move
+// 4 consecutive floats at a time (heads (4t + j) % H, fixed per thread since 1024 is a multiple
+// of H); otherwise one float at a time.
 template <int H>
 __global__ __launch_bounds__(kBlock) void softmax_hub_write_kernel(const int32_t* __restrict__ row_ptr,
                                                                    const float* sc, float* out, PlanView plan) {
+    __shared__ float lm[kWavesPerBlock][H], lz[kWavesPerBlock][H];
+    __shared__ float gM[H], gR[H];   // the row's max and 1 / sum per head
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int n_hub_segs = plan.counts[kNHubSegs];
     const bool wide = H >= 4 && ((reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
     for (int s = blockIdx.x; s < n_hub_segs; s += gridDim.x) {
         const int4 sg = plan.segs[s];   // row, b, e, slot (= s)
-        const int rb = row_ptr[sg.x];
+        const int rb = row_ptr[sg.x], re = row_ptr[sg.x + 1];
         const int first = sg.w - (int)(((int64_t)sg.y - rb) / plan.seg_len);
-        const float* p0 = plan.partials + (int64_t)first * plan.state_floats;
+        const int nseg = (int)(((int64_t)re - rb + plan.seg_len - 1) / plan.seg_len);
+        // the row's state: per-thread merge over its segments, then the tree over the workgroup
+        const int h = t % H;
+        float m = -INFINITY, z = 0.f;
+        for (int c = t / H; c < nseg; c += kBlock / H) {
+            const float* pc = plan.partials + (int64_t)(first + c) * plan.state_floats;
+            merge_state(m, z, pc[h], pc[H + h]);
+        }
+#pragma unroll
+        for (int o = H; o < kWave; o <<= 1) {
+            const float mo = shfl_xor(m, o), zo = shfl_xor(z, o);
+            merge_state(m, z, mo, zo);
+        }
+        if (lane < H) {
+            lm[w][lane] = m;
+            lz[w][lane] = z;
+        }
+        __syncthreads();
+        if (t < H) {
+            float M = lm[0][t], Z = lz[0][t];
+#pragma unroll
+            for (int i = 1; i < kWavesPerBlock; ++i) merge_state(M, Z, lm[i][t], lz[i][t]);
+            gM[t] = M;
+            gR[t] = 1.f / Z;
+        }
+        __syncthreads();
         const int64_t beg = (int64_t)sg.y * H, end = (int64_t)sg.z * H;
         if (wide) {
             constexpr int NB = kHubBatch / 4;   // float4 per thread per batch
             const float4* s4 = reinterpret_cast<const float4*>(sc + beg);
             float4* o4 = reinterpret_cast<float4*>(out + beg);
             const int64_t n4 = (end - beg) / 4;   // H >= 4: whole float4s
-            for (int64_t f0 = threadIdx.x; f0 < n4; f0 += NB * kBlock) {
+            const int h0 = (4 * t) % H;
+            float M[4], rz[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                M[j] = gM[(h0 + j) % H];
+                rz[j] = gR[(h0 + j) % H];
+            }
+            for (int64_t f0 = t; f0 < n4; f0 += NB * kBlock) {
                 float4 v[NB];
 #pragma unroll
                 for (int k = 0; k < NB; ++k) {
                     const int64_t f = f0 + (int64_t)k * kBlock;
                     v[k] = f < n4 ? s4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-                const int h0 = (4 * threadIdx.x) % H;
-                float M[4], rz[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    M[j] = p0[(h0 + j) % H];
-                    rz[j] = 1.f / p0[H + (h0 + j) % H];
                 }
 #pragma unroll
                 for (int k = 0; k < NB; ++k) {
@@ -355,24 +446,24 @@ __global__ __launch_bounds__(kBlock) void softmax_hub_write_kernel(const int32_t
                                             exp_fast(v[k].z - M[2]) * rz[2], exp_fast(v[k].w - M[3]) * rz[3]);
                 }
             }
-            continue;
-        }
-        // kBlock is a multiple of H, so every element this thread touches has head t % H
-        const int h = threadIdx.x % H;
-        for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += kHubBatch * kBlock) {
-            float v[kHubBatch];
+        } else {
+            // kBlock is a multiple of H, so every element this thread touches has head t % H
+            const float M = gM[h], rz = gR[h];
+            for (int64_t i0 = beg + t; i0 < end; i0 += kHubBatch * kBlock) {
+                float v[kHubBatch];
 #pragma unroll
-            for (int k = 0; k < kHubBatch; ++k) {
-                const int64_t i = i0 + (int64_t)k * kBlock;
-                v[k] = i < end ? sc[i] : 0.f;
-            }
-            const float M = p0[h], rz = 1.f / p0[H + h];
+                for (int k = 0; k < kHubBatch; ++k) {
+                    const int64_t i = i0 + (int64_t)k * kBlock;
+                    v[k] = i < end ? sc[i] : 0.f;
+                }
 #pragma unroll
-            for (int k = 0; k < kHubBatch; ++k) {
-                const int64_t i = i0 + (int64_t)k * kBlock;
-                if (i < end) out[i] = exp_fast(v[k] - M) * rz;
+                for (int k = 0; k < kHubBatch; ++k) {
+                    const int64_t i = i0 + (int64_t)k * kBlock;
+                    if (i < end) out[i] = exp_fast(v[k] - M) * rz;
+                }
             }
         }
+        __syncthreads();   // gM / gR and lm / lz are rewritten for the next segment
     }
 }
 
@@ -384,10 +475,8 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         constexpr int HH = decltype(tag)::H;
         const int short_max = plan ? plan->short_max : INT32_MAX;
         const int staged = short_max < kBlkBudget / HH ? short_max : kBlkBudget / HH;   // rows the stage takes
-        if (plan)
-            hipLaunchKernelGGL(softmax_segment_kernel<HH>,
-                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kSegmentGrid)),
-                               dim3(kBlock), 0, stream, scores, out, *plan);
+        // Disjoint rows: the staged and slot kernels first, then the plan's segments (read from the
+        // end of the table), then the hub alpha pass, which starts with the hub scores read last.
         int64_t rpw = (n_rows + kSmFillWaves - 1) / kSmFillWaves;   // enough waves to fill the device
         rpw = rpw < 1 ? 1 : (rpw > kBlkRows ? kBlkRows : rpw);
         const int64_t bwaves = (n_rows + rpw - 1) / rpw;
@@ -398,13 +487,14 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
             hipLaunchKernelGGL(softmax_short_kernel<HH>, dim3(grid_for(waves, kWavesPerBlock, INT32_MAX)),
                                dim3(kBlock), 0, stream, row_ptr, n_rows, scores, out, staged, short_max);
         }
-        if (plan) {
-            hipLaunchKernelGGL(softmax_hub_merge_kernel<HH>, dim3(grid_for(plan->hub_capacity, 1, kPersistentBlocks)),
-                               dim3(kBlock), 0, stream, *plan);
+        if (plan)
+            hipLaunchKernelGGL(softmax_segment_kernel<HH>,
+                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kSegmentGrid)),
+                               dim3(kBlock), 0, stream, scores, out, *plan);
+        if (plan)
             hipLaunchKernelGGL(softmax_hub_write_kernel<HH>,
                                dim3(grid_for(plan->hubseg_capacity, 1, kSegmentGrid)), dim3(kBlock), 0, stream,
                                row_ptr, scores, out, *plan);
-        }
     });
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
