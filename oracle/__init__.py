@@ -65,6 +65,7 @@ class Oracle:
         L.oracle_softmax_aggregate.argtypes = [i64, vp, vp, i32, i32, vp, vp, i32, vp]
         L.oracle_layer.argtypes = [i64, vp, vp, i32, i32, vp, vp, vp, i32, dbl, vp]
         L.oracle_edge_softmax_backward.argtypes = [i64, vp, i32, vp, vp, vp]
+        L.oracle_sddmm_backward.argtypes = [i64, vp, vp, vp, i64, vp, i64, i32, i32, i32, dbl, vp, vp, vp]
         L.oracle_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
         L.oracle_softmax_aggregate_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, i32, vp, vp, vp]
         L.oracle_layer_backward.argtypes = [i64, vp, vp, i32, i32, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp]
@@ -149,6 +150,25 @@ class Oracle:
 
 
     # --- backward (derivatives of the steps above) --------------------------------------
+    def sddmm_backward(self, src_idx, dst_idx, src_feat, dst_feat, grad, scale: float = 1.0):
+        """(dL/dsrc_feat [n_src,H,D], dL/ddst_feat [n_dst,H,D]) of sddmm from dL/dout [E,H]."""
+        src_idx = np.ascontiguousarray(src_idx, np.int32)
+        dst_idx = np.ascontiguousarray(dst_idx, np.int32)
+        src_feat = np.ascontiguousarray(src_feat)
+        dst_feat = np.ascontiguousarray(dst_feat)
+        grad = np.ascontiguousarray(grad, np.float64)
+        assert src_feat.dtype == dst_feat.dtype and src_feat.ndim == 3 and dst_feat.ndim == 3
+        ns, H, D = src_feat.shape
+        nd = dst_feat.shape[0]
+        assert dst_feat.shape[1:] == (H, D) and grad.shape == (src_idx.size, H) and dst_idx.size == src_idx.size
+        d_src = np.full((ns, H, D), np.nan, np.float64)
+        d_dst = np.full((nd, H, D), np.nan, np.float64)
+        rc = self.lib.oracle_sddmm_backward(src_idx.size, _p(src_idx), _p(dst_idx), _p(src_feat), ns, _p(dst_feat),
+                                            nd, _dtype_code(src_feat), H, D, float(scale), _p(grad), _p(d_src),
+                                            _p(d_dst))
+        assert rc == 0
+        return d_src, d_dst
+
     def edge_softmax_backward(self, row_ptr, alpha, grad) -> np.ndarray:
         """dL/dscores from the softmax output alpha and dL/dalpha, both [E,H]."""
         row_ptr = np.ascontiguousarray(row_ptr, np.int32)

@@ -215,6 +215,41 @@ int oracle_layer(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
  * ------------------------------------------------------------------------------------------ */
 
 /*
+ * SDDMM backward over an edge list, g = dL/dout [n_edges,heads] of oracle_sddmm:
+ *   d_dst[dst_idx[e],h,d] = sum over edges e of scale * g[e,h] * src_feat[src_idx[e],h,d]
+ *   d_src[src_idx[e],h,d] = sum over edges e of scale * g[e,h] * dst_feat[dst_idx[e],h,d]
+ * The l1_p10 page notes that the gradients accumulate into the rows of the two feature tables the
+ * edges read.  Both outputs start at 0.0 (rows no edge reads stay +0.0); every sum visits the
+ * edges in increasing edge id.  Threads split (output table, head) pairs, so no two write one
+ * value.
+ */
+int oracle_sddmm_backward(int64_t n_edges, const int32_t* src_idx, const int32_t* dst_idx,
+                          const void* src_feat, int64_t n_src, const void* dst_feat, int64_t n_dst, int dtype,
+                          int heads, int head_dim, double scale, const double* grad, double* d_src,
+                          double* d_dst)
+{
+    for (int64_t x = 0; x < n_src * heads * head_dim; ++x)
+        d_src[x] = 0.0;
+    for (int64_t x = 0; x < n_dst * heads * head_dim; ++x)
+        d_dst[x] = 0.0;
+#pragma omp parallel for schedule(static)
+    for (int task = 0; task < 2 * heads; ++task) {
+        int h = task / 2;
+        int to_dst = task % 2;   /* 1: d_dst (reads src_feat); 0: d_src (reads dst_feat) */
+        for (int64_t e = 0; e < n_edges; ++e) {
+            double w = scale * grad[e * heads + h];
+            int64_t out_row = to_dst ? dst_idx[e] : src_idx[e];
+            int64_t in_row = to_dst ? src_idx[e] : dst_idx[e];
+            const void* in = to_dst ? src_feat : dst_feat;
+            double* out = to_dst ? d_dst : d_src;
+            for (int d = 0; d < head_dim; ++d)
+                out[(out_row * heads + h) * head_dim + d] += w * load_feat(in, dtype, (in_row * heads + h) * head_dim + d);
+        }
+    }
+    return 0;
+}
+
+/*
  * Edge softmax backward: for every row i with edges and every head h, with a = softmax output
  * and g = dL/da over the row's edges:
  *   out[e,h] = a[e,h] * (g[e,h] - sum_{e' in row i} a[e',h] * g[e',h])

@@ -315,6 +315,46 @@ def pin_backward_finite_differences(orc):
     _fd_check(f, X, dv)
 
 
+def pin_sddmm_backward(orc):
+    """COO SDDMM gradients: against the dense products scale * G_h @ Src_h (d_dst) and
+    scale * G_h^T @ Dst_h (d_src), G_h[i,j] summing g[e,h] over the edges i <- j (numpy matmul, with
+    repeated edges); against central differences of the forward oracle; exact integer products
+    bitwise; rows no edge reads are +0.0."""
+    r = _rng(36)
+    for H, D, scale in [(1, 5, 1.0), (3, 4, 0.6)]:
+        ns, nd, E = 9, 7, 40
+        src_idx = r.integers(0, ns - 1, E).astype(np.int32)   # the last source row is never read
+        dst_idx = r.integers(1, nd, E).astype(np.int32)       # nor the first destination row
+        src_idx[:3] = src_idx[0]                              # repeated (dst, src) pairs
+        dst_idx[:3] = dst_idx[0]
+        S, T = r.standard_normal((ns, H, D)), r.standard_normal((nd, H, D))
+        g = r.standard_normal((E, H))
+        d_src, d_dst = orc.sddmm_backward(src_idx, dst_idx, S, T, g, scale=scale)
+        for h in range(H):
+            Gd = np.zeros((nd, ns))
+            np.add.at(Gd, (dst_idx, src_idx), g[:, h])
+            np.testing.assert_allclose(d_dst[:, h, :], scale * (Gd @ S[:, h, :]), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(d_src[:, h, :], scale * (Gd.T @ T[:, h, :]), rtol=1e-12, atol=1e-12)
+        for arr in (d_src[ns - 1], d_dst[0]):
+            assert np.all(arr == 0.0) and not np.any(np.signbit(arr))
+        f = lambda: float((orc.sddmm(src_idx, dst_idx, S, T, scale=scale) * g).sum())  # noqa: E731
+        _fd_check(f, S, d_src)
+        _fd_check(f, T, d_dst)
+    # integer-valued tables (bf16) and upstream gradients: exact sums, bitwise against int64 products
+    H, D, ns, nd, E = 2, 16, 11, 6, 70
+    src_idx = r.integers(0, ns, E).astype(np.int32)
+    dst_idx = r.integers(0, nd, E).astype(np.int32)
+    Si = r.integers(-8, 9, (ns, H, D)).astype(np.float32)
+    Ti = r.integers(-8, 9, (nd, H, D)).astype(np.float32)
+    gi = r.integers(-4, 5, (E, H)).astype(np.float64)
+    d_src, d_dst = orc.sddmm_backward(src_idx, dst_idx, G.f32_to_bf16_bits(Si), G.f32_to_bf16_bits(Ti), gi)
+    for h in range(H):
+        Gd = np.zeros((nd, ns), np.int64)
+        np.add.at(Gd, (dst_idx, src_idx), gi[:, h].astype(np.int64))
+        assert np.array_equal(d_dst[:, h, :], (Gd @ Si[:, h, :].astype(np.int64)).astype(np.float64))
+        assert np.array_equal(d_src[:, h, :], (Gd.T @ Ti[:, h, :].astype(np.int64)).astype(np.float64))
+
+
 def _dense_layer_autograd(g, Q, K, V, Go, scale):
     """torch autograd (fp64, CPU) of dense per-head attention over each row's edge multiset:
     A[i,j] = C[i,j] exp(S[i,j] - m_i) / sum_j C[i,j] exp(S[i,j] - m_i), S = scale Q K^T, where C
@@ -511,7 +551,7 @@ def pin_linear_closed_forms(orc):
 ALL_PINS = [pin_sddmm_dense, pin_sddmm_integer_exact, pin_softmax_closed_forms, pin_softmax_dense,
             pin_softmax_invariants, pin_aggregate_dense, pin_aggregate_integer_exact,
             pin_zero_rows_positive_zero, pin_softmax_aggregate_dense, pin_softmax_aggregate_closed_forms,
-            pin_layer_dense, pin_backward_finite_differences, pin_layer_backward_autograd,
+            pin_layer_dense, pin_backward_finite_differences, pin_sddmm_backward, pin_layer_backward_autograd,
             pin_backward_invariants, pin_aggregate_backward_integer_exact, pin_relation_attention_torch,
             pin_relation_attention_closed_forms, pin_linear_torch, pin_linear_integer_exact,
             pin_linear_closed_forms]

@@ -65,6 +65,12 @@ MUTANTS = [
     ("layer_bwd_dk_reads_k", "scale * gs[e * heads + h] * load_feat(q, dtype, (i * heads + h) * head_dim + d);",
      "scale * gs[e * heads + h] * load_feat(k, dtype, (j * heads + h) * head_dim + d);"),
     ("layer_bwd_dv_weights_are_scores", "n_src, a, v, dtype, grad, ga, dv);", "n_src, s, v, dtype, grad, ga, dv);"),
+    ("sddmm_bwd_scale_dropped", "double w = scale * grad[e * heads + h];", "double w = grad[e * heads + h];"),
+    ("sddmm_bwd_grad_head0", "double w = scale * grad[e * heads + h];", "double w = scale * grad[e * heads];"),
+    ("sddmm_bwd_dsrc_reads_src", "const void* in = to_dst ? src_feat : dst_feat;",
+     "const void* in = to_dst ? src_feat : src_feat;"),
+    ("sddmm_bwd_input_head_dropped", "load_feat(in, dtype, (in_row * heads + h) * head_dim + d)",
+     "load_feat(in, dtype, (in_row * heads) * head_dim + d)"),
     ("softagg_bwd_weights_are_scores", "n_src, alpha, feat, dtype, grad, ga, dfeat);",
      "n_src, scores, feat, dtype, grad, ga, dfeat);"),
     # dense relation-biased attention block
