@@ -389,7 +389,11 @@ def bench_coo(args, w, gat, G):
     import torch
     si, di, sf, df = G.make_coo(w, args.seed)
     dev = torch.device("cuda:0")
-    t = lambda a: torch.from_numpy(a).to(dev)
+    def t(a):   # uint16 arrays are bfloat16 bit patterns
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
     sid, did, sfd, dfd = t(si), t(di), t(sf), t(df)
     E, H, D = w.n_edges, w.heads, w.head_dim
     out = torch.empty((E, H), dtype=torch.float32, device=dev)
@@ -414,7 +418,35 @@ def bench_coo(args, w, gat, G):
     b0.record(stream)
     torch.cuda.synchronize()
     t_b2b_us = a0.elapsed_time(b0)
-    alg = 8 * E + 2 * E * H * D * 4 + 4 * E * H
+    fb = 2 if w.dtype == "bf16" else 4
+    alg = 8 * E + 2 * E * H * D * fb + 4 * E * H
+    extra = {"t_sddmm_ms": t_k * 1e3, "sddmm_alg_bytes": alg, "sddmm_back_to_back_us": t_b2b_us}
+    grad = None
+    if args.backward:
+        grad = torch.from_numpy(np.random.default_rng(args.seed + 1).standard_normal((E, H)).astype(np.float32)).to(dev)
+        ws = torch.empty(gat.gat_sddmm_backward_workspace_bytes(E, w.n_src, w.n_dst, H, D), dtype=torch.uint8,
+                         device=dev)
+        d_src = torch.empty((w.n_src, H, D), dtype=torch.float32, device=dev)
+        d_dst = torch.empty((w.n_dst, H, D), dtype=torch.float32, device=dev)
+        bwd = lambda: gat.gat_sddmm_backward(sid, did, sfd, dfd, grad, ws=ws, d_src=d_src, d_dst=d_dst)  # noqa: E731
+        for _ in range(max(1, args.warmup)):
+            bwd()
+        evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evb:
+            a.record(stream)
+            bwd()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t_bwd = float(np.mean([a.elapsed_time(b) for a, b in evb])) * 1e-3
+        # per edge: both indices, the gradient and one gathered row of each table; per row: one output row
+        bwd_alg = 8 * E + 4 * E * H + 2 * E * H * D * fb + (w.n_src + w.n_dst) * H * D * 4
+        bwd_unique = 8 * E + 4 * E * H + (w.n_src + w.n_dst) * H * D * (fb + 4)
+        extra.update({"t_sddmm_backward_ms": t_bwd * 1e3, "sddmm_backward_alg_bytes": bwd_alg,
+                      "sddmm_backward_gbs": bwd_alg / t_bwd / 1e9,
+                      "sddmm_backward_unique_bytes": bwd_unique,
+                      "sddmm_backward_unique_gbs": bwd_unique / t_bwd / 1e9,
+                      "sddmm_backward_edge_heads_per_s": E * H / t_bwd})
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -427,6 +459,14 @@ def bench_coo(args, w, gat, G):
         cpu = {"value": E * H / dt, "unit": "edge-heads/s", "cores": orc.num_threads(), "kind": "oracle",
                "host": host_cpu(),
                "sample": f"the whole edge list ({E} edges), {reps} repetitions"}
+        if grad is not None:
+            gh = grad.cpu().numpy()
+            reps, t1 = 0, time.perf_counter()
+            while time.perf_counter() - t1 < 3.0:
+                orc.sddmm_backward(si, di, sf, df, gh)
+                reps += 1
+            extra["cpu_sddmm_backward_edge_heads_per_s"] = E * H / ((time.perf_counter() - t1) / reps)
+            extra["cpu_sddmm_backward_sample"] = f"the whole edge list, both gradients, {reps} repetitions"
     print(json.dumps({
         "metric": METRIC, "value": E * H / (elapsed / args.steps), "unit": "edge-heads/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
@@ -434,9 +474,10 @@ def bench_coo(args, w, gat, G):
         "config": {"workload": w.description, "n_edges": E, "n_src": w.n_src, "n_dst": w.n_dst, "heads": H,
                    "head_dim": D, "features": w.dtype, "seed": args.seed, "step": "sddmm over the edge list"},
         "roofline": {"bound": "hbm", "achieved": alg / t_k / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": alg / t_k / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "sddmm (launch-bound size)"},
+                     "frac": alg / t_k / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "sddmm (launch-bound size)" if E < (1 << 20) else "sddmm"},
         "cpu_baseline": cpu,
-        "extra": {"t_sddmm_ms": t_k * 1e3, "sddmm_alg_bytes": alg, "sddmm_back_to_back_us": t_b2b_us},
+        "extra": extra,
     }))
 
 
@@ -445,15 +486,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "relation", "projection"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "coo24", "c3", "c4", "c5", "relation",
+                                                                "projection"])
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "gather"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--batch", type=int, default=1, help="graphs of the workload (seeds seed..seed+B-1) "
                                                           "batched as one block-diagonal graph")
-    ap.add_argument("--backward", action="store_true", help="also time the transposed-graph build and the "
-                                                              "full-layer backward")
+    ap.add_argument("--backward", action="store_true", help="also time the backward: the transposed-graph "
+                    "build and the full-layer backward (CSR workloads), the SDDMM backward (COO workloads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -382,6 +382,36 @@ gat_status gat_fused_layer_backward(const int32_t* row_ptr, const int32_t* col_i
                                     const gat_plan* plan, const gat_csc* csc, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
 
+/* Workspace bytes for gat_sddmm_backward (0 if the sizes or shape are unsupported). */
+size_t gat_sddmm_backward_workspace_bytes(int64_t n_edges, int64_t n_src, int64_t n_dst, int heads,
+                                          int head_dim);
+
+/*
+ * SDDMM backward (derivative of gat_sddmm, the edge-only SDDMM of [l1_p10]; its backward-pass
+ * passage: each edge's gradient flows into the two feature rows it read).  With grad_out =
+ * dL/dout fp32 [n_edges,heads]:
+ *   d_src[i,h,:] = scale * sum over the edges e with src_idx[e] = i of grad_out[e,h] * dst_feat[dst_idx[e],h,:]
+ *   d_dst[j,h,:] = scale * sum over the edges e with dst_idx[e] = j of grad_out[e,h] * src_feat[src_idx[e],h,:]
+ * d_src fp32 [n_src,heads,head_dim] and d_dst fp32 [n_dst,heads,head_dim] may each be NULL (not
+ * computed); rows that no edge reads get +0.0.  Repeated (src, dst) pairs are separate terms.
+ * Each gradient is an aggregation over the edges grouped by one endpoint: the call sorts the
+ * edge ids by that endpoint (stable radix passes on the device), builds the grouping's row
+ * offsets and plan in `ws`, and sums each row in registers, so no atomic addition is used and
+ * the result does not depend on the launch.  scale * grad_out is rounded to fp32 before it is
+ * multiplied; sums are fp32.
+ * ws: device workspace of at least gat_sddmm_backward_workspace_bytes(...) bytes, 256-byte
+ * aligned (GAT_ERR_ARGS otherwise), owned by the caller; its contents need no clearing and are
+ * scratch after the call.  Calls sharing ws must be ordered on one stream.  n_src or n_dst = 0
+ * with n_edges > 0 is GAT_ERR_ARGS; src_feat must be given when d_dst is asked for and dst_feat
+ * when d_src is (GAT_ERR_NULL).  Requires 0 <= src_idx[e] < n_src and 0 <= dst_idx[e] < n_dst
+ * (not checked on the device).
+ */
+gat_status gat_sddmm_backward(const int32_t* src_idx, const int32_t* dst_idx, int64_t n_edges,
+                              const void* src_feat, int64_t n_src, const void* dst_feat, int64_t n_dst,
+                              gat_dtype dtype, int heads, int head_dim, float scale,
+                              const float* grad_out, float* d_src, float* d_dst,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -231,6 +231,49 @@ BwdLayout bwd_layout(int64_t n_edges, int heads) {
     return B;
 }
 
+// COO SDDMM backward workspace.  The two gradients are sums over the edges grouped by one
+// endpoint; each side in turn sorts the edges by that endpoint (stable radix passes), builds
+// the CSR of the grouping and its plan, and runs the aggregation.  Both sides reuse the same
+// buffers, sized for the larger side.
+struct CooBwdLayout {
+    size_t off_row_ptr, off_col, off_keys[2], off_vals[2], off_hist, off_sums, off_w, off_plan, total;
+    size_t plan_bytes;
+};
+
+int radix_passes(int64_t n_keys) {
+    int bits = 0;
+    while (bits < 31 && ((int64_t)1 << bits) < n_keys) ++bits;   // keys are < n_keys
+    const int p = (bits + gat::kRadixDigitBits - 1) / gat::kRadixDigitBits;
+    return p < 1 ? 1 : p;
+}
+
+CooBwdLayout coo_bwd_layout(int64_t n_edges, int64_t n_src, int64_t n_dst, int heads, int head_dim) {
+    CooBwdLayout C{};
+    const int64_t n_max = n_src > n_dst ? n_src : n_dst;
+    const int64_t hist = (int64_t)gat::kRadixDigits * gat::radix_tiles(n_edges);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    C.off_row_ptr = take((size_t)(n_max + 1) * 4);
+    C.off_col = take((size_t)n_edges * 4);
+    for (int b = 0; b < 2; ++b) {
+        C.off_keys[b] = take((size_t)n_edges * 4);
+        C.off_vals[b] = take((size_t)n_edges * 4);
+    }
+    C.off_hist = take((size_t)hist * 4);
+    C.off_sums = take((size_t)(gat::scan_tiles(hist) + 1) * 4);
+    C.off_w = take((size_t)n_edges * heads * 4);
+    const size_t ps = plan_layout(n_src, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN).total;
+    const size_t pd = plan_layout(n_dst, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN).total;
+    C.plan_bytes = ps > pd ? ps : pd;
+    C.off_plan = take(C.plan_bytes);
+    C.total = off;
+    return C;
+}
+
 }  // namespace
 
 extern "C" {
@@ -547,7 +590,7 @@ gat_status gat_aggregate_backward(const int32_t* row_ptr, const int32_t* col_idx
     if (e == hipSuccess && dfeat && n_src > 0) {
         const int32_t* perm = at<int32_t>(csc, csc->off_perm);
         float* stage = at<float>(csc, csc->off_stage);
-        e = gat::launch_permute_edges(heads, perm, weights, n_edges, stage, stream);
+        e = gat::launch_permute_edges(heads, perm, weights, n_edges, 1.f, stage, stream);
         const gat::PlanView pv = plan_view(&csc->plan);
         if (e == hipSuccess)
             e = gat::launch_spmm(gat::kAgg, GAT_F32, heads, head_dim, at<int32_t>(csc, csc->off_col_ptr),
@@ -611,7 +654,7 @@ gat_status gat_fused_layer_backward(const int32_t* row_ptr, const int32_t* col_i
         if (e == hipSuccess)
             e = gat::launch_softmax_backward(heads, row_ptr, n_rows, alpha, g, layer ? g : dscores,
                                              layer ? scale : 1.f, &pv, stream);
-        if (e == hipSuccess) e = gat::launch_permute_edges(heads, perm, alpha, n_edges, stage, stream);
+        if (e == hipSuccess) e = gat::launch_permute_edges(heads, perm, alpha, n_edges, 1.f, stage, stream);
     }
     // dv over the transposed graph (+0.0 for sources no edge reads)
     if (e == hipSuccess && n_src > 0)
@@ -621,10 +664,80 @@ gat_status gat_fused_layer_backward(const int32_t* row_ptr, const int32_t* col_i
         if (e == hipSuccess && n_rows > 0)
             e = gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, row_ptr, col_idx, n_rows, n_src, g, nullptr,
                                  nullptr, k, 1.f, dq, &pv, stream);
-        if (e == hipSuccess && n_edges > 0) e = gat::launch_permute_edges(heads, perm, g, n_edges, stage, stream);
+        if (e == hipSuccess && n_edges > 0)
+            e = gat::launch_permute_edges(heads, perm, g, n_edges, 1.f, stage, stream);
         if (e == hipSuccess && n_src > 0)
             e = gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, col_ptr, row_idx, n_src, n_rows, stage, nullptr,
                                  nullptr, q, 1.f, dk, &cv, stream);
+    }
+    return hip_status(e);
+}
+
+size_t gat_sddmm_backward_workspace_bytes(int64_t n_edges, int64_t n_src, int64_t n_dst, int heads, int head_dim) {
+    if (!edges_ok(n_edges) || !size_ok(n_src) || !size_ok(n_dst) || !shape_ok(heads, head_dim)) return 0;
+    return coo_bwd_layout(n_edges, n_src, n_dst, heads, head_dim).total;
+}
+
+gat_status gat_sddmm_backward(const int32_t* src_idx, const int32_t* dst_idx, int64_t n_edges, const void* src_feat,
+                              int64_t n_src, const void* dst_feat, int64_t n_dst, gat_dtype dtype, int heads,
+                              int head_dim, float scale, const float* grad_out, float* d_src, float* d_dst, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    if (!edges_ok(n_edges) || !size_ok(n_src) || !size_ok(n_dst)) return GAT_ERR_SIZE;
+    if (!shape_ok(heads, head_dim) || !dtype_ok(dtype)) return GAT_ERR_UNSUPPORTED;
+    if (ws == nullptr) return GAT_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return GAT_ERR_ARGS;
+    const CooBwdLayout C = coo_bwd_layout(n_edges, n_src, n_dst, heads, head_dim);
+    if (ws_bytes < C.total) return GAT_ERR_WORKSPACE;
+    if (n_edges > 0) {
+        if (n_src == 0 || n_dst == 0) return GAT_ERR_ARGS;   // an edge needs a source and a destination row
+        if (!src_idx || !dst_idx || !grad_out) return GAT_ERR_NULL;
+        if ((d_src && !dst_feat) || (d_dst && !src_feat)) return GAT_ERR_NULL;
+    }
+    char* base = static_cast<char*>(ws);
+    auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+    int32_t* row_ptr = I(C.off_row_ptr);
+    int32_t* col = I(C.off_col);
+    float* w = reinterpret_cast<float*>(base + C.off_w);
+    // side 0: d_dst, edges grouped by dst_idx, gathering src_feat; side 1: d_src, grouped by src_idx, gathering
+    // dst_feat.  An output of a side with no rows, or not asked for, is skipped.
+    struct Side {
+        float* out;
+        const int32_t* key;
+        const int32_t* other;
+        int64_t n_rows, n_other;
+        const void* feat;
+    };
+    const Side sides[2] = {{d_dst, dst_idx, src_idx, n_dst, n_src, src_feat},
+                           {d_src, src_idx, dst_idx, n_src, n_dst, dst_feat}};
+    hipError_t e = hipSuccess;
+    for (const Side& sd : sides) {
+        if (sd.out == nullptr || sd.n_rows == 0) continue;
+        // stable LSD passes over the key bits: (key, edge id) ends sorted by key, then edge id.  With no
+        // edges the passes enqueue nothing, row_ptr is all zeros and the aggregation writes +0.0 rows.
+        const int passes = radix_passes(sd.n_rows);
+        for (int pass = 0; e == hipSuccess && pass < passes; ++pass) {
+            const int32_t* kin = pass == 0 ? sd.key : I(C.off_keys[(pass - 1) % 2]);
+            const int32_t* vin = pass == 0 ? nullptr : I(C.off_vals[(pass - 1) % 2]);
+            e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), n_edges,
+                                       pass * gat::kRadixDigitBits, I(C.off_hist), I(C.off_sums), stream);
+        }
+        const int32_t* perm = I(C.off_vals[(passes - 1) % 2]);
+        if (e == hipSuccess)
+            e = gat::launch_csc_finish(I(C.off_keys[(passes - 1) % 2]), perm, sd.other, n_edges, sd.n_rows, row_ptr,
+                                       col, stream);
+        if (e == hipSuccess) e = gat::launch_permute_edges(heads, perm, grad_out, n_edges, scale, w, stream);
+        gat_plan plan;
+        const Layout L =
+            plan_layout(sd.n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN);
+        if (e == hipSuccess)
+            e = build_plan(row_ptr, sd.n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN, L,
+                           base + C.off_plan, C.plan_bytes, &plan, stream);
+        if (e == hipSuccess) {
+            const gat::PlanView pv = plan_view(&plan);
+            e = gat::launch_spmm(gat::kAgg, dtype, heads, head_dim, row_ptr, col, sd.n_rows, sd.n_other, w, nullptr,
+                                 nullptr, sd.feat, 1.f, sd.out, &pv, stream);
+        }
+        if (e != hipSuccess) break;
     }
     return hip_status(e);
 }

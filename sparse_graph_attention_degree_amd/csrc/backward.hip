@@ -218,20 +218,26 @@ __global__ __launch_bounds__(kBlock) void gather_rows_kernel(const int32_t* __re
         row_idx[p] = rows[perm[p]];
 }
 
-// dst[p,:] = src[perm[p],:] for [E,H] per-edge values
+// dst[p,:] = scale * src[perm[p],:] for [E,H] per-edge values (scale 1 moves the bits unchanged)
 template <int H>
 __global__ __launch_bounds__(kBlock) void permute_edges_kernel(const int32_t* __restrict__ perm,
                                                                const float* __restrict__ src, int64_t n,
-                                                               float* __restrict__ dst) {
+                                                               float scale, float* __restrict__ dst) {
     for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n; p += (int64_t)gridDim.x * kBlock) {
         const int64_t e = perm[p];
         if constexpr (H % 4 == 0) {
 #pragma unroll
-            for (int h = 0; h < H; h += 4)
-                *reinterpret_cast<float4*>(dst + p * H + h) = *reinterpret_cast<const float4*>(src + e * H + h);
+            for (int h = 0; h < H; h += 4) {
+                float4 x = *reinterpret_cast<const float4*>(src + e * H + h);
+                x.x *= scale;
+                x.y *= scale;
+                x.z *= scale;
+                x.w *= scale;
+                *reinterpret_cast<float4*>(dst + p * H + h) = x;
+            }
         } else {
 #pragma unroll
-            for (int h = 0; h < H; ++h) dst[p * H + h] = src[e * H + h];
+            for (int h = 0; h < H; ++h) dst[p * H + h] = scale * src[e * H + h];
         }
     }
 }
@@ -526,13 +532,13 @@ hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const in
     return hipGetLastError();
 }
 
-hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float* dst,
+hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float scale, float* dst,
                                 hipStream_t stream) {
     if (n == 0) return hipSuccess;
     const bool ok = dispatch_heads(H, [&](auto tag) {
         constexpr int HH = decltype(tag)::H;
         hipLaunchKernelGGL(permute_edges_kernel<HH>, dim3(grid_for(n, kBlock, 65536)), dim3(kBlock), 0, stream, perm,
-                           src, n, dst);
+                           src, n, scale, dst);
     });
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();

@@ -120,7 +120,8 @@ hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* ko
 hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
                              int64_t n_src, int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
 
-hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float* dst,
+// dst[p,:] = scale * src[perm[p],:], [E,H] fp32
+hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float scale, float* dst,
                                 hipStream_t stream);
 
 // out[e,h] = <G[rows[e],h,:], F[col[e],h,:]>, G fp32 [*,H,D], F of dtype

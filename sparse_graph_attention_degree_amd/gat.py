@@ -29,7 +29,8 @@ EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge
             "gat_csc_workspace_bytes", "gat_csc_sizeof", "gat_csc_build", "gat_edge_softmax_backward",
             "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward",
             "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block", "gat_linear",
-            "gat_fused_layer_noalloc", "gat_fused_layer_noalloc_bytes"]
+            "gat_fused_layer_noalloc", "gat_fused_layer_noalloc_bytes", "gat_sddmm_backward_workspace_bytes",
+            "gat_sddmm_backward"]
 
 
 class GatError(RuntimeError):
@@ -93,6 +94,9 @@ def _lib():
     L.gat_layer_backward_workspace_bytes.restype = sz
     L.gat_fused_layer_backward.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, f32, vp, vp,
                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gat_sddmm_backward_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.gat_sddmm_backward_workspace_bytes.restype = sz
+    L.gat_sddmm_backward.argtypes = [vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.gat_batch_csr.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     L.gat_relation_block_lds_bytes.argtypes = [i32, i32, i32, i32]
     L.gat_relation_block_lds_bytes.restype = sz
@@ -101,6 +105,7 @@ def _lib():
     for f in (L.gat_plan_build, L.gat_sddmm, L.gat_edge_softmax, L.gat_aggregate, L.gat_fused_layer,
               L.gat_fused_layer_noalloc,
               L.gat_csc_build, L.gat_edge_softmax_backward, L.gat_aggregate_backward, L.gat_fused_layer_backward,
+              L.gat_sddmm_backward,
               L.gat_batch_csr, L.gat_relation_block, L.gat_linear):
         f.restype = i32
     L.gat_status_str.argtypes = [i32]
@@ -418,6 +423,49 @@ def gat_fused_layer_backward(row_ptr, col_idx, v, grad_out, plan: Plan, csc: Csc
                                            _ptr(grad_out), _ptr(dscores), _ptr(dq), _ptr(dk), _ptr(dv), plan.ref(),
                                            csc.ref(), _ptr(ws), ws.numel(), _stream(stream)))
     return dscores, dq, dk, dv
+
+
+def gat_sddmm_backward_workspace_bytes(n_edges, n_src, n_dst, heads, head_dim) -> int:
+    return int(_lib().gat_sddmm_backward_workspace_bytes(n_edges, n_src, n_dst, heads, head_dim))
+
+
+def gat_sddmm_backward(src_idx, dst_idx, src_feat, dst_feat, grad_out, scale: float = 1.0, need_src=True,
+                       need_dst=True, ws: torch.Tensor | None = None, d_src=None, d_dst=None, stream=None):
+    """Gradients of gat_sddmm with respect to src_feat and dst_feat, fp32 [n,H,D] (None where not
+    asked for): d_src[i] = scale * sum_{src_idx[e]=i} grad_out[e] * dst_feat[dst_idx[e]], and
+    d_dst likewise."""
+    _dev(src_idx, "src_idx", torch.int32, 1)
+    _dev(dst_idx, "dst_idx", torch.int32, 1)
+    _dev(src_feat, "src_feat", None, 3)
+    _dev(dst_feat, "dst_feat", src_feat.dtype, 3)
+    _dev(grad_out, "grad_out", torch.float32, 2)
+    E = src_idx.numel()
+    (ns, H, D), nd = src_feat.shape, dst_feat.shape[0]
+    if dst_idx.numel() != E or dst_feat.shape[1:] != src_feat.shape[1:] or tuple(grad_out.shape) != (E, H):
+        raise ValueError("inconsistent sddmm backward shapes")
+    dev = src_feat.device
+    need = gat_sddmm_backward_workspace_bytes(E, ns, nd, H, D)
+    if need == 0:
+        raise GatError("gat_sddmm_backward_workspace_bytes", 2)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(ws, "ws", torch.uint8, 1)
+    if need_src and d_src is None:
+        d_src = torch.empty((ns, H, D), dtype=torch.float32, device=dev)
+    if need_dst and d_dst is None:
+        d_dst = torch.empty((nd, H, D), dtype=torch.float32, device=dev)
+    d_src = d_src if need_src else None
+    d_dst = d_dst if need_dst else None
+    _dev(d_src, "d_src", torch.float32, 3)
+    _dev(d_dst, "d_dst", torch.float32, 3)
+    if (d_src is not None and tuple(d_src.shape) != (ns, H, D)) or (d_dst is not None and
+                                                                  tuple(d_dst.shape) != (nd, H, D)):
+        raise ValueError("gradient outputs must be [n_src|n_dst, H, D]")
+    _check("gat_sddmm_backward",
+           _lib().gat_sddmm_backward(_ptr(src_idx), _ptr(dst_idx), E, _ptr(src_feat), ns, _ptr(dst_feat), nd,
+                                     _feat_dtype(src_feat), H, D, float(scale), _ptr(grad_out), _ptr(d_src),
+                                     _ptr(d_dst), _ptr(ws), ws.numel(), _stream(stream)))
+    return d_src, d_dst
 
 
 # ----------------------------------------------------------------------------- batching

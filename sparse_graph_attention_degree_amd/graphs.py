@@ -225,6 +225,8 @@ WORKLOADS = {
                    description="csr softmax+aggregate, 1 head: 384 rows, Poisson(18), 384x64 fp32"),
     "c2": Workload("c2", "coo", 1, 128, "f32", n_src=1024, n_dst=768, n_edges=16384,
                    description="coo sddmm: 1024x128 / 768x128 fp32, 16384 edges"),
+    "coo24": Workload("coo24", "coo", 4, 32, "bf16", n_src=2**18, n_dst=2**18, n_edges=2**24,
+                      description="coo sddmm at scale: 2^18 x 4x32 / 2^18 x 4x32 bf16, 2^24 uniform edges"),
     "c3": Workload("c3", "csr", 8, 32, "f32", n_rows=16384, n_src=16384, degree="poisson",
                    params=dict(mean=18.0), score_std=2.0,
                    description="multi-head softmax+aggregate: 16384 rows, Poisson(18), 8x32 fp32"),

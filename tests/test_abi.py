@@ -151,6 +151,35 @@ def test_noalloc_host_checks(L):
     assert L.gat_fused_layer_noalloc_bytes(4, 5, 3, 64) == 0
 
 
+def test_sddmm_backward_host_checks(L):
+    """COO SDDMM backward: every argument check fails on the host, before anything is enqueued."""
+    f, wsb = L.gat_sddmm_backward, L.gat_sddmm_backward_workspace_bytes
+    need = wsb(16384, 1024, 768, 1, 128)
+    # at least: the two radix key/value buffers, the grouping's columns and the scaled gradient
+    assert need >= 16384 * 4 * 5 + 16384 * 1 * 4
+    assert wsb(-1, 4, 4, 1, 64) == 0 and wsb(5, 2**31, 4, 1, 64) == 0 and wsb(5, 4, 4, 3, 64) == 0
+    assert wsb(0, 0, 0, 1, 64) > 0
+
+    def call(E=10, ns=4, nd=4, dt=0, H=1, D=64, src=FAKE, dst=FAKE, sf=FAKE, df=FAKE, g=FAKE, ds=FAKE, dd=FAKE,
+             ws=FAKE, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = wsb(max(E, 0), max(ns, 0), max(nd, 0), H, D) if wsb(E, ns, nd, H, D) else 1 << 30
+        return f(src, dst, E, sf, ns, df, nd, dt, H, D, 1.0, g, ds, dd, ws, ws_bytes, None)
+
+    assert call(E=-1) == SIZE and call(ns=2**31) == SIZE and call(nd=-3) == SIZE
+    assert call(H=3) == UNSUP and call(D=48) == UNSUP and call(H=16, D=128) == UNSUP and call(dt=7) == UNSUP
+    assert call(ws=None) == NULL
+    assert call(ws=ctypes.c_void_p(0x1010)) == ARGS                 # not 256-byte aligned
+    assert call(ws_bytes=wsb(10, 4, 4, 1, 64) - 1) == WS
+    assert call(ns=0) == ARGS and call(nd=0) == ARGS                # an edge needs both endpoints
+    assert call(src=None) == NULL and call(dst=None) == NULL and call(g=None) == NULL
+    assert call(df=None) == NULL                                    # d_src gathers dst_feat
+    assert call(sf=None) == NULL                                    # d_dst gathers src_feat
+    # nothing asked for, or no rows on either side: nothing to enqueue
+    assert call(E=0, ns=0, nd=0, src=None, dst=None, g=None) == OK
+    assert call(E=0, ds=None, dd=None, src=None, dst=None, g=None, sf=None, df=None) == OK
+
+
 def test_plan_refused_for_another_row_ptr(L):
     """A plan is tied to the row_ptr array it was built from: a call with another array of the same
     sizes is refused on the host (it would leave the rows the plan does not cover unwritten)."""
