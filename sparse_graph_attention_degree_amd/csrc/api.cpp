@@ -164,7 +164,7 @@ hipError_t build_plan(const int32_t* row_ptr, int64_t n_rows, int64_t n_edges, i
 constexpr uint32_t kCscMagic = 0x47415443u;   // "GATC"
 
 struct CscLayout {
-    int sort_passes;
+    gat::RadixPlan sort;
     size_t off_col_ptr, off_row_idx, off_rows, off_keys[2], off_vals[2], off_hist, off_sums, off_stage, off_plan;
     Layout plan;
     size_t total;
@@ -173,11 +173,8 @@ struct CscLayout {
 CscLayout csc_layout(int64_t n_rows, int64_t n_src, int64_t n_edges, int heads, int head_dim) {
     (void)n_rows;
     CscLayout C{};
-    int bits = 0;
-    while (bits < 31 && ((int64_t)1 << bits) < n_src) ++bits;   // columns are < n_src
-    C.sort_passes = (bits + gat::kRadixDigitBits - 1) / gat::kRadixDigitBits;
-    if (C.sort_passes < 1) C.sort_passes = 1;
-    const int64_t hist = (int64_t)gat::kRadixDigits * gat::radix_tiles(n_edges);
+    C.sort = gat::radix_plan(n_src);   // columns are < n_src
+    const int64_t hist = (int64_t)gat::kRadixMaxBins * gat::radix_tiles(n_edges);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -240,17 +237,10 @@ struct CooBwdLayout {
     size_t plan_bytes;
 };
 
-int radix_passes(int64_t n_keys) {
-    int bits = 0;
-    while (bits < 31 && ((int64_t)1 << bits) < n_keys) ++bits;   // keys are < n_keys
-    const int p = (bits + gat::kRadixDigitBits - 1) / gat::kRadixDigitBits;
-    return p < 1 ? 1 : p;
-}
-
 CooBwdLayout coo_bwd_layout(int64_t n_edges, int64_t n_src, int64_t n_dst, int heads, int head_dim) {
     CooBwdLayout C{};
     const int64_t n_max = n_src > n_dst ? n_src : n_dst;
-    const int64_t hist = (int64_t)gat::kRadixDigits * gat::radix_tiles(n_edges);
+    const int64_t hist = (int64_t)gat::kRadixMaxBins * gat::radix_tiles(n_edges);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -531,19 +521,19 @@ gat_status gat_csc_build(const int32_t* row_ptr, const int32_t* col_idx, int64_t
     c.off_row_idx = C.off_row_idx;
     c.off_rows = C.off_rows;
     c.off_stage = C.off_stage;
-    c.off_perm = C.off_vals[(C.sort_passes - 1) % 2];
+    c.off_perm = C.off_vals[(C.sort.passes - 1) % 2];
     char* base = static_cast<char*>(ws);
     auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
     hipError_t e = gat::launch_expand_rows(row_ptr, n_rows, I(C.off_rows), stream);
     // stable LSD passes over the column bits: (column, edge id) ends sorted by column, then edge id
-    for (int pass = 0; e == hipSuccess && pass < C.sort_passes; ++pass) {
+    for (int pass = 0; e == hipSuccess && pass < C.sort.passes; ++pass) {
         const int32_t* kin = pass == 0 ? col_idx : I(C.off_keys[(pass - 1) % 2]);
         const int32_t* vin = pass == 0 ? nullptr : I(C.off_vals[(pass - 1) % 2]);
         e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), n_edges,
-                                   pass * gat::kRadixDigitBits, I(C.off_hist), I(C.off_sums), stream);
+                                   pass * C.sort.bits, C.sort.bits, I(C.off_hist), I(C.off_sums), stream);
     }
     if (e == hipSuccess)
-        e = gat::launch_csc_finish(I(C.off_keys[(C.sort_passes - 1) % 2]), I(c.off_perm), I(C.off_rows), n_edges,
+        e = gat::launch_csc_finish(I(C.off_keys[(C.sort.passes - 1) % 2]), I(c.off_perm), I(C.off_rows), n_edges,
                                    n_src, I(C.off_col_ptr), I(C.off_row_idx), stream);
     if (e == hipSuccess)
         e = build_plan(I(C.off_col_ptr), n_src, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN,
@@ -714,18 +704,17 @@ gat_status gat_sddmm_backward(const int32_t* src_idx, const int32_t* dst_idx, in
         if (sd.out == nullptr || sd.n_rows == 0) continue;
         // stable LSD passes over the key bits: (key, edge id) ends sorted by key, then edge id.  With no
         // edges the passes enqueue nothing, row_ptr is all zeros and the aggregation writes +0.0 rows.
-        const int passes = radix_passes(sd.n_rows);
-        for (int pass = 0; e == hipSuccess && pass < passes; ++pass) {
+        const gat::RadixPlan rp = gat::radix_plan(sd.n_rows);
+        for (int pass = 0; e == hipSuccess && pass < rp.passes; ++pass) {
             const int32_t* kin = pass == 0 ? sd.key : I(C.off_keys[(pass - 1) % 2]);
             const int32_t* vin = pass == 0 ? nullptr : I(C.off_vals[(pass - 1) % 2]);
             e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), n_edges,
-                                       pass * gat::kRadixDigitBits, I(C.off_hist), I(C.off_sums), stream);
+                                       pass * rp.bits, rp.bits, I(C.off_hist), I(C.off_sums), stream);
         }
-        const int32_t* perm = I(C.off_vals[(passes - 1) % 2]);
+        const int32_t* perm = I(C.off_vals[(rp.passes - 1) % 2]);
         if (e == hipSuccess)
-            e = gat::launch_csc_finish(I(C.off_keys[(passes - 1) % 2]), perm, sd.other, n_edges, sd.n_rows, row_ptr,
-                                       col, stream);
-        if (e == hipSuccess) e = gat::launch_permute_edges(heads, perm, grad_out, n_edges, scale, w, stream);
+            e = gat::launch_group_finish(heads, I(C.off_keys[(rp.passes - 1) % 2]), perm, sd.other, grad_out, scale,
+                                         n_edges, sd.n_rows, row_ptr, col, w, stream);
         gat_plan plan;
         const Layout L =
             plan_layout(sd.n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN);

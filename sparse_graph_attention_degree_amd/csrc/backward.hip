@@ -9,9 +9,9 @@
 //
 // Kernels in this file:
 //  * expand_rows: row id of every CSR edge.
-//  * radix_hist / radix_scatter: one pass of an LSD radix sort (4-bit digits) of (column, edge
-//    id) pairs, stable, so the final order is by column and then by edge id; scan_*: the
-//    exclusive scan of the per-tile digit counts between the two.
+//  * radix_hist / radix_scatter: one pass of an LSD radix sort (digits of up to 8 bits) of
+//    (column, edge id) pairs, stable, so the final order is by column and then by edge id; scan_*:
+//    the exclusive scan of the per-tile digit counts between the two.
 //  * csc_bounds: column pointers from the sorted columns; gather_rows: row id per CSC entry.
 //  * permute_edges: per-edge values [E,H] moved into CSC order.
 //  * edge_dot: per edge and head, <G[row(e)], F[col(e)]> with G fp32 and F fp32 or bf16 (the
@@ -53,78 +53,114 @@ __global__ __launch_bounds__(kBlock) void expand_rows_kernel(const int32_t* __re
 }
 
 // ------------------------------------------------------------------------------ radix sort
-// A tile is kSortItems consecutive keys per thread: thread t owns items t*16 .. t*16+15 of the
-// tile, so a stable rank is (same-digit items of threads < t) + (same-digit items earlier in t).
-constexpr int kRadixBins = kRadixDigits;
+// One LSD pass on a digit of `bits` <= 8 bits.  A tile is 4096 consecutive items, 1024 per wave in
+// 16 rounds of 64 (round k, lane l: item k*64 + l of the wave's run).  In each round the lanes
+// holding the same digit find each other with one ballot per digit bit; a lane's stable rank in the
+// wave is the wave's running count of its digit (LDS) plus the same-digit lanes below it.  After
+// the rounds the per-wave counts give each digit's start in the tile, the items are placed in LDS in
+// (digit, rank) order, and the tile is written out in that order: consecutive threads write
+// consecutive positions of one digit's run, so the stores are coalesced runs instead of one scattered
+// 4-byte store per item.
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kBlock * kSortItems;
+constexpr int kWaveRun = kSortTile / kWavesPerBlock;
 
 __global__ __launch_bounds__(kBlock) void radix_hist_kernel(const int32_t* __restrict__ keys, int64_t n, int shift,
-                                                            int32_t* __restrict__ hist, int64_t n_tiles) {
-    __shared__ int cnt[kRadixBins];
+                                                            int bits, int32_t* __restrict__ hist, int64_t n_tiles) {
+    __shared__ int cnt[kRadixMaxBins];
     const int t = threadIdx.x;
-    if (t < kRadixBins) cnt[t] = 0;
+    const int bins = 1 << bits, mask = bins - 1;
+    cnt[t] = 0;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
 #pragma unroll
     for (int k = 0; k < kSortItems; ++k) {
         const int64_t i = base + (int64_t)k * kBlock + t;
-        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & (kRadixBins - 1)], 1);
+        if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & mask], 1);
     }
     __syncthreads();
-    if (t < kRadixBins) hist[(int64_t)t * n_tiles + blockIdx.x] = cnt[t];
+    if (t < bins) hist[(int64_t)t * n_tiles + blockIdx.x] = cnt[t];
 }
 
+__device__ int block_exscan_int(int v, int& total);
+
 // vin == nullptr: the values are the item positions (the first pass, identity order).
+// offs[d * n_tiles + tile]: the output position of the tile's first item of digit d.
 __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const int32_t* __restrict__ kin,
                                                                const int32_t* __restrict__ vin,
                                                                int32_t* __restrict__ kout, int32_t* __restrict__ vout,
-                                                               int64_t n, int shift, const int32_t* __restrict__ offs,
-                                                               int64_t n_tiles) {
-    __shared__ int cnt[kRadixBins][kBlock];       // per digit, per thread: count, then rank base
-    __shared__ int chunk[kRadixBins][kBlock / 16];
-    const int t = threadIdx.x;
-    const int64_t i0 = (int64_t)blockIdx.x * kSortTile + (int64_t)t * kSortItems;
-    int key[kSortItems];
+                                                               int64_t n, int shift, int bits,
+                                                               const int32_t* __restrict__ offs, int64_t n_tiles) {
+    __shared__ int wcnt[kWavesPerBlock][kRadixMaxBins];   // per wave and digit: count, then the wave's base
+    __shared__ int dstart[kRadixMaxBins];                   // digit's first slot in the tile
+    __shared__ int dglobal[kRadixMaxBins];                  // output position of slot 0 of the digit's run
+    __shared__ int skey[kSortTile], sval[kSortTile];
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    const int bins = 1 << bits, mask = bins - 1;
+    const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;
+    const int64_t run0 = tile0 + (int64_t)w * kWaveRun;
+    const uint64_t below_me = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
-    for (int k = 0; k < kSortItems; ++k) key[k] = i0 + k < n ? kin[i0 + k] : 0;
-#pragma unroll
-    for (int d = 0; d < kRadixBins; ++d) cnt[d][t] = 0;
-#pragma unroll
-    for (int k = 0; k < kSortItems; ++k)
-        if (i0 + k < n) cnt[(key[k] >> shift) & (kRadixBins - 1)][t] += 1;
+    for (int wv = 0; wv < kWavesPerBlock; ++wv) wcnt[wv][t] = 0;
     __syncthreads();
-    // exclusive scan of cnt[d][0..255] for every digit: 16 threads per digit scan 16 entries each,
-    // then one thread per digit scans the 16 chunk sums
-    {
-        const int d = t / 16, ch = t % 16;
-        int s = 0;
-        for (int j = 0; j < 16; ++j) {
-            const int v = cnt[d][ch * 16 + j];
-            cnt[d][ch * 16 + j] = s;
-            s += v;
+    int key[kSortItems], val[kSortItems], rank[kSortItems];
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const int64_t i = run0 + (int64_t)k * kWave + lane;
+        const bool valid = i < n;
+        key[k] = valid ? kin[i] : 0;
+        val[k] = valid ? (vin ? vin[i] : (int32_t)i) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const bool valid = run0 + (int64_t)k * kWave + lane < n;
+        const int d = (key[k] >> shift) & mask;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < bits; ++b) {
+            const uint64_t set = __ballot((d >> b) & 1);
+            peers &= ((d >> b) & 1) ? set : ~set;
         }
-        chunk[d][ch] = s;
+        const int below = __popcll(peers & below_me);
+        const int before = wcnt[w][d];
+        rank[k] = before + below;
+        wave_lds_handoff();   // every lane has read the counts before the run's first lane bumps them
+        if (valid && below == 0) wcnt[w][d] = before + __popcll(peers);
+        wave_lds_handoff();
     }
     __syncthreads();
-    if (t < kRadixBins) {
-        int s = 0;
-        for (int ch = 0; ch < 16; ++ch) {
-            const int v = chunk[t][ch];
-            chunk[t][ch] = s;
-            s += v;
+    // digit t: the waves' bases within the digit (in wave order), then the digit's start in the tile
+    int tot = 0;
+    if (t < bins) {
+#pragma unroll
+        for (int wv = 0; wv < kWavesPerBlock; ++wv) {
+            const int c = wcnt[wv][t];
+            wcnt[wv][t] = tot;
+            tot += c;
         }
+    }
+    int all;
+    const int ex = block_exscan_int(t < bins ? tot : 0, all);
+    if (t < bins) {
+        dstart[t] = ex;
+        dglobal[t] = offs[(int64_t)t * n_tiles + blockIdx.x] - ex;
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kSortItems; ++k) {
-        if (i0 + k < n) {
-            const int d = (key[k] >> shift) & (kRadixBins - 1);
-            const int64_t pos = (int64_t)offs[(int64_t)d * n_tiles + blockIdx.x] + chunk[d][t / 16] + cnt[d][t];
-            cnt[d][t] += 1;   // only this thread touches column t
-            kout[pos] = key[k];
-            vout[pos] = vin ? vin[i0 + k] : (int32_t)(i0 + k);
+        if (run0 + (int64_t)k * kWave + lane < n) {
+            const int d = (key[k] >> shift) & mask;
+            const int slot = dstart[d] + wcnt[w][d] + rank[k];
+            skey[slot] = key[k];
+            sval[slot] = val[k];
         }
+    }
+    __syncthreads();
+    const int tile_n = (int)(n - tile0 < kSortTile ? n - tile0 : kSortTile);
+    for (int i = t; i < tile_n; i += kBlock) {
+        const int kk = skey[i];
+        const int64_t pos = (int64_t)dglobal[(kk >> shift) & mask] + i;
+        kout[pos] = kk;
+        vout[pos] = sval[i];
     }
 }
 
@@ -238,6 +274,34 @@ __global__ __launch_bounds__(kBlock) void permute_edges_kernel(const int32_t* __
         } else {
 #pragma unroll
             for (int h = 0; h < H; ++h) dst[p * H + h] = scale * src[e * H + h];
+        }
+    }
+}
+
+// The entries of an edge list grouped by one endpoint (perm: edge id per sorted position):
+// col[p] = other[perm[p]] and w[p,:] = scale * grad[perm[p],:], [E,H] fp32, in one pass over perm.
+template <int H>
+__global__ __launch_bounds__(kBlock) void gather_entries_kernel(const int32_t* __restrict__ perm,
+                                                                const int32_t* __restrict__ other,
+                                                                const float* __restrict__ grad, int64_t n,
+                                                                float scale, int32_t* __restrict__ col,
+                                                                float* __restrict__ w) {
+    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n; p += (int64_t)gridDim.x * kBlock) {
+        const int64_t e = perm[p];
+        col[p] = other[e];
+        if constexpr (H % 4 == 0) {
+#pragma unroll
+            for (int h = 0; h < H; h += 4) {
+                float4 x = *reinterpret_cast<const float4*>(grad + e * H + h);
+                x.x *= scale;
+                x.y *= scale;
+                x.z *= scale;
+                x.w *= scale;
+                *reinterpret_cast<float4*>(w + p * H + h) = x;
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < H; ++h) w[p * H + h] = scale * grad[e * H + h];
         }
     }
 }
@@ -511,15 +575,25 @@ hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* sums, in
 }
 
 hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout, int64_t n,
-                             int shift, int32_t* hist, int32_t* sums, hipStream_t stream) {
+                             int shift, int bits, int32_t* hist, int32_t* sums, hipStream_t stream) {
     if (n == 0) return hipSuccess;
+    if (bits < 1 || bits > kRadixMaxBits || shift < 0 || shift > 30) return hipErrorInvalidValue;
     const int64_t nt = radix_tiles(n);
-    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, n, shift, hist, nt);
-    const hipError_t e = launch_exclusive_scan(hist, nt * kRadixBins, sums, hist, stream);
+    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, n, shift, bits, hist, nt);
+    const hipError_t e = launch_exclusive_scan(hist, nt << bits, sums, hist, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, vin, kout, vout, n,
-                       shift, hist, nt);
+                       shift, bits, hist, nt);
     return hipGetLastError();
+}
+
+RadixPlan radix_plan(int64_t n_keys) {
+    int bits = 0;
+    while (bits < 31 && ((int64_t)1 << bits) < n_keys) ++bits;   // keys are < n_keys
+    RadixPlan p;
+    p.passes = bits == 0 ? 1 : (bits + kRadixMaxBits - 1) / kRadixMaxBits;
+    p.bits = bits == 0 ? 1 : (bits + p.passes - 1) / p.passes;
+    return p;
 }
 
 hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
@@ -529,6 +603,21 @@ hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const in
     if (n_edges > 0)
         hipLaunchKernelGGL(gather_rows_kernel, dim3(grid_for(n_edges, kBlock, 65536)), dim3(kBlock), 0, stream, perm,
                            rows, n_edges, row_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_finish(int H, const int32_t* skeys, const int32_t* perm, const int32_t* other,
+                               const float* grad, float scale, int64_t n_edges, int64_t n_rows, int32_t* row_ptr,
+                               int32_t* col, float* w, hipStream_t stream) {
+    hipLaunchKernelGGL(csc_bounds_kernel, dim3(grid_for(n_edges + 1, kBlock, 65536)), dim3(kBlock), 0, stream, skeys,
+                       n_edges, n_rows, row_ptr);
+    if (n_edges == 0) return hipGetLastError();
+    const bool ok = dispatch_heads(H, [&](auto tag) {
+        constexpr int HH = decltype(tag)::H;
+        hipLaunchKernelGGL(gather_entries_kernel<HH>, dim3(grid_for(n_edges, kBlock, 65536)), dim3(kBlock), 0, stream,
+                           perm, other, grad, n_edges, scale, col, w);
+    });
+    if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

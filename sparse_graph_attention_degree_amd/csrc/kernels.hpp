@@ -108,17 +108,30 @@ hipError_t launch_expand_rows(const int32_t* row_ptr, int64_t n_rows, int32_t* r
 // radix sort of (column, edge id): tiles per pass, and tiles of the scan of the digit counts
 int64_t radix_tiles(int64_t n);
 int64_t scan_tiles(int64_t n);
-constexpr int kRadixDigitBits = 4;
-constexpr int kRadixDigits = 1 << kRadixDigitBits;
+constexpr int kRadixMaxBits = 8;
+constexpr int kRadixMaxBins = 1 << kRadixMaxBits;
 
-// one stable pass on bits [shift, shift+4) of the keys; vin == nullptr means values = positions.
-// hist: int32 [16 * radix_tiles(n)], sums: int32 [scan_tiles(16 * radix_tiles(n))].
+// LSD passes for keys in [0, n_keys): `passes` digits of `bits` bits each (bits <= 8, as even as
+// possible; one 1-bit pass for n_keys <= 1).
+struct RadixPlan {
+    int passes, bits;
+};
+RadixPlan radix_plan(int64_t n_keys);
+
+// one stable pass on bits [shift, shift+bits) of the keys; vin == nullptr means values = positions.
+// hist: int32 [256 * radix_tiles(n)], sums: int32 [scan_tiles(256 * radix_tiles(n)) + 1].
 hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout, int64_t n,
-                             int shift, int32_t* hist, int32_t* sums, hipStream_t stream);
+                             int shift, int bits, int32_t* hist, int32_t* sums, hipStream_t stream);
 
 // col_ptr [n_src+1] from the sorted columns; row_idx[p] = rows[perm[p]]
 hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
                              int64_t n_src, int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
+
+// An edge list grouped by one endpoint, from the sorted keys (< n_rows) and perm of the radix passes:
+// row_ptr [n_rows+1], col[p] = other[perm[p]], w[p,:] = scale * grad[perm[p],:] ([E,H] fp32).
+hipError_t launch_group_finish(int H, const int32_t* skeys, const int32_t* perm, const int32_t* other,
+                               const float* grad, float scale, int64_t n_edges, int64_t n_rows, int32_t* row_ptr,
+                               int32_t* col, float* w, hipStream_t stream);
 
 // dst[p,:] = scale * src[perm[p],:], [E,H] fp32
 hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float scale, float* dst,
