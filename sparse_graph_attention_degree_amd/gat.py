@@ -394,8 +394,10 @@ def gat_layer_backward_workspace_bytes(n_edges, heads) -> int:
 
 
 def gat_fused_layer_backward(row_ptr, col_idx, v, grad_out, plan: Plan, csc: Csc, scores=None, q=None, k=None,
-                             scale: float = 1.0, ws: torch.Tensor | None = None, stream=None):
-    """Gradients of gat_fused_layer: (dscores, None, None, dv) with scores, or (None, dq, dk, dv) with q, k."""
+                             scale: float = 1.0, ws: torch.Tensor | None = None, stream=None, dscores=None, dq=None,
+                             dk=None, dv=None):
+    """Gradients of gat_fused_layer: (dscores, None, None, dv) with scores, or (None, dq, dk, dv) with q, k.
+    The output tensors may be supplied (those the mode does not use are ignored)."""
     for t, name in ((row_ptr, "row_ptr"), (col_idx, "col_idx")):
         _dev(t, name, torch.int32, 1)
     _dev(v, "v", None, 3)
@@ -413,10 +415,21 @@ def gat_fused_layer_backward(row_ptr, col_idx, v, grad_out, plan: Plan, csc: Csc
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _dev(ws, "ws", torch.uint8, 1)
     layer = scores is None
-    dscores = None if layer else torch.empty((E, H), dtype=torch.float32, device=dev)
-    dq = torch.empty((n_rows, H, D), dtype=torch.float32, device=dev) if layer else None
-    dk = torch.empty((ns, H, D), dtype=torch.float32, device=dev) if layer else None
-    dv = torch.empty((ns, H, D), dtype=torch.float32, device=dev)
+
+    def output(t, shape, used):
+        if not used:
+            return None
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=dev)
+        _dev(t, "gradient output", torch.float32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"gradient output is {tuple(t.shape)}, expected {shape}")
+        return t
+
+    dscores = output(dscores, (E, H), not layer)
+    dq = output(dq, (n_rows, H, D), layer)
+    dk = output(dk, (ns, H, D), layer)
+    dv = output(dv, (ns, H, D), True)
     _check("gat_fused_layer_backward",
            _lib().gat_fused_layer_backward(_ptr(row_ptr), _ptr(col_idx), n_rows, ns, E, H, D, _feat_dtype(v),
                                            _ptr(scores), _ptr(q), _ptr(k), float(scale), _ptr(v),
@@ -469,7 +482,7 @@ def gat_sddmm_backward(src_idx, dst_idx, src_feat, dst_feat, grad_out, scale: fl
 
 
 # ----------------------------------------------------------------------------- batching
-def gat_batch_csr(local_row_ptr, local_col, row_off, edge_off, src_off, stream=None):
+def gat_batch_csr(local_row_ptr, local_col, row_off, edge_off, src_off, stream=None, row_ptr=None, col=None):
     """Block-diagonal CSR of B graphs from their concatenated arrays and int32 offsets [B+1]
     (prefix sums of rows, edges and sources); returns (row_ptr, col_idx)."""
     for t, name in ((local_row_ptr, "local_row_ptr"), (local_col, "local_col"), (row_off, "row_off"),
@@ -480,8 +493,14 @@ def gat_batch_csr(local_row_ptr, local_col, row_off, edge_off, src_off, stream=N
         raise ValueError("offset arrays differ in length")
     n_rows = local_row_ptr.numel() - B
     n_edges = local_col.numel()
-    row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=row_off.device)
-    col = torch.empty(n_edges, dtype=torch.int32, device=row_off.device)
+    if row_ptr is None:
+        row_ptr = torch.empty(n_rows + 1, dtype=torch.int32, device=row_off.device)
+    if col is None:
+        col = torch.empty(n_edges, dtype=torch.int32, device=row_off.device)
+    _dev(row_ptr, "row_ptr", torch.int32, 1)
+    _dev(col, "col", torch.int32, 1)
+    if row_ptr.numel() != n_rows + 1 or col.numel() != n_edges:
+        raise ValueError("output arrays of the wrong size")
     _check("gat_batch_csr", _lib().gat_batch_csr(_ptr(local_row_ptr), _ptr(local_col), _ptr(row_off),
                                                  _ptr(edge_off), _ptr(src_off), B, n_rows, n_edges, _ptr(row_ptr),
                                                  _ptr(col), _stream(stream)))

@@ -67,7 +67,7 @@ def test_linear_matches_oracle(case, x_dtype, y_dtype):
     M, K, N, n_out = case
     x, w, b = G.make_linear(M, K, N, seed=M + K + N, x_dtype=x_dtype, bias=M % 2 == 0)
     got = _run(x, w, b, n_out, y_dtype)
-    _check(got, x, w, b, "f32" if y_dtype == torch.float32 else "bf16", f"linear {case} {x_dtype}")
+    _check(got, x, w, b, "f32" if y_dtype == torch.float32 else "bf16_out", f"linear {case} {x_dtype}")
 
 
 def test_bf16_output_is_the_rounded_fp32_output():
@@ -161,7 +161,7 @@ def test_full_size_projections_sampled(which):
     M, K = p["M"], p["K"]
     if which == "qkv":
         x, w, b = G.make_linear(M, K, 3 * K, seed=12, x_dtype="bf16", bias=False)
-        n_out, y_dtype, kind = 3, torch.bfloat16, "bf16"
+        n_out, y_dtype, kind = 3, torch.bfloat16, "bf16_out"
     else:
         x, w, b = G.make_linear(M, K, K, seed=13, x_dtype="f32", bias=True)
         n_out, y_dtype, kind = 1, torch.float32, "f32"
@@ -178,8 +178,8 @@ def test_full_size_projections_sampled(which):
 def test_projected_layer_end_to_end():
     """q, k, v = x Wqkv^T (bf16, the layer's input dtype); o = graph attention layer; y = o Wo^T + bo,
     on a graph with every degree class (and rows without edges, whose y is the bias); against the
-    oracle's projections and layer in fp64.  The bf16 roundings of q/k/v and o are inside the
-    bf16 tolerance."""
+    oracle's projections and layer in fp64.  q/k/v are rounded to bf16 mid-path on the GPU and
+    not in the oracle, a quantisation the exp of the softmax amplifies: the contract bound only."""
     H, D = 4, 64
     F = H * D
     g = mixed_graph(41, n_rows=400, n_src=400, hubs=(2500,))
@@ -198,6 +198,6 @@ def test_projected_layer_end_to_end():
     o64 = orc.layer(g.row_ptr, g.col_idx, q64, k64, v64, scale).reshape(n, F)
     want = orc.linear(o64, wo, bo.astype(np.float64))
     mag = orc.linear(np.abs(o64), np.abs(_f64(wo)), np.abs(bo.astype(np.float64)))
-    assert_close_sum(y, want, mag, "bf16", "projected layer")
+    assert_close_sum(y, want, mag, "bf16_chain", "projected layer")
     empty = g.degrees() == 0
     assert empty.any() and np.array_equal(y[empty], np.broadcast_to(bo, (int(empty.sum()), F)))

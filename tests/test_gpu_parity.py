@@ -13,7 +13,8 @@ import oracle
 import oracle.binning as B
 from sparse_graph_attention_degree_amd import gat
 from sparse_graph_attention_degree_amd import graphs as G
-from tests.gpu_helpers import assert_close, assert_positive_zero_rows, mixed_graph, to_dev, to_np
+from tests.gpu_helpers import (abs_feat, assert_close, assert_guard, assert_positive_zero_rows, guarded, mixed_graph,
+                               to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,7 +99,8 @@ def test_fused_softmax_aggregate(orc, H, D, dt, sched):
     out = gat.gat_fused_layer(rp, col, to_dev(x), scores=to_dev(s), plan=_plan(rp, g.n_edges, H, D, sched))
     got = to_np(out)
     want = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, x)
-    assert_close(got, want, dt, "fused softmax+aggregate")
+    mag = orc.softmax_aggregate(g.row_ptr, g.col_idx, s, abs_feat(x))
+    assert_close(got, want, dt, "fused softmax+aggregate", mag)
     assert_positive_zero_rows(got, g.degrees())
 
 
@@ -113,7 +115,8 @@ def test_aggregate(orc, H, D, dt, sched):
     out = gat.gat_aggregate(rp, col, to_dev(w), to_dev(x), plan=_plan(rp, g.n_edges, H, D, sched))
     got = to_np(out)
     want = orc.aggregate(g.row_ptr, g.col_idx, w, x)
-    assert_close(got, want, dt, "aggregate")
+    mag = orc.aggregate(g.row_ptr, g.col_idx, np.abs(w), abs_feat(x))
+    assert_close(got, want, dt, "aggregate", mag)
     assert_positive_zero_rows(got, g.degrees())
 
 
@@ -129,7 +132,8 @@ def test_full_layer(orc, H, D, dt, sched):
                               plan=_plan(rp, g.n_edges, H, D, sched))
     got = to_np(out)
     want = orc.layer(g.row_ptr, g.col_idx, q, k, v, scale=qs)
-    assert_close(got, want, dt, "full layer")
+    mag = orc.layer(g.row_ptr, g.col_idx, q, k, abs_feat(v), scale=qs)
+    assert_close(got, want, dt, "full layer", mag)
     assert_positive_zero_rows(got, g.degrees())
 
 
@@ -184,7 +188,8 @@ def test_sddmm(orc, H, D, dt):
     a, b = _feat(r, nd, H, D, dt), _feat(r, ns, H, D, dt)
     out = gat.gat_sddmm(to_dev(si), to_dev(di), to_dev(b), to_dev(a), scale=0.5)
     want = orc.sddmm(si, di, b, a, scale=0.5)
-    assert_close(to_np(out), want, dt, "sddmm")
+    mag = orc.sddmm(si, di, abs_feat(b), abs_feat(a), scale=0.5)
+    assert_close(to_np(out), want, dt, "sddmm", mag)
 
 
 # --------------------------------------------------------------------------------------- workloads
@@ -242,11 +247,13 @@ def test_c4_layer_full_size(orc):
     rows = G.sample_rows(g, 512, 1)
     sub_rp, sub_col, eids = G.take_rows(g, rows)
     want = orc.layer(sub_rp, sub_col, q[rows], k, v)
-    assert_close(to_np(chain)[rows], want, "bf16", "c4 chain")
-    assert_close(to_np(fused)[rows], want, "bf16", "c4 fused layer")
+    mag = orc.layer(sub_rp, sub_col, q[rows], k, abs_feat(v))
+    assert_close(to_np(chain)[rows], want, "bf16", "c4 chain", mag)
+    assert_close(to_np(fused)[rows], want, "bf16", "c4 fused layer", mag)
     s_want = orc.sddmm(sub_col, G.row_of_edge(sub_rp), k, q[rows])
+    s_mag = orc.sddmm(sub_col, G.row_of_edge(sub_rp), abs_feat(k), abs_feat(q[rows]))
     s_got = to_np(scores)[eids]
-    assert_close(s_got, s_want, "bf16", "c4 sddmm")
+    assert_close(s_got, s_want, "bf16", "c4 sddmm", s_mag)
 
 
 @pytest.mark.timeout(400)
@@ -430,4 +437,5 @@ def test_c4_aggregate_full_size(orc):
     out = to_np(gat.gat_aggregate(rp, col, to_dev(wts), to_dev(x), plan=plan))
     rows = G.sample_rows(g, 512, 4)
     sub_rp, sub_col, eids = G.take_rows(g, rows)
-    assert_close(out[rows], orc.aggregate(sub_rp, sub_col, wts[eids], x), "bf16", "c4 aggregate")
+    mag = orc.aggregate(sub_rp, sub_col, np.abs(wts[eids]), abs_feat(x))
+    assert_close(out[rows], orc.aggregate(sub_rp, sub_col, wts[eids], x), "bf16", "c4 aggregate", mag)
