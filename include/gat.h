@@ -412,6 +412,16 @@ gat_status gat_sddmm_backward(const int32_t* src_idx, const int32_t* dst_idx, in
                               const float* grad_out, float* d_src, float* d_dst,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Testing hook.  The edge-parallel kernels (gat_sddmm and the edge dot products of the backward)
+ * launch one wave per step of edges, up to 2^23 workgroups, and loop over the edges with a
+ * grid stride past that (2^29 edges and up).  This caps their workgroups at `cap` so that the
+ * loop runs at sizes a test can check; cap <= 0 or above 2^23 restores the default.  Returns the
+ * previous cap.  Process-wide, host only; launches already enqueued keep their grid.  Every
+ * edge's result is bitwise the same at any cap.
+ * ------------------------------------------------------------------------------------------ */
+int64_t gat_testing_edge_grid_cap(int64_t cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.hpp"
 #include "linear.hpp"
 
@@ -264,9 +266,19 @@ CooBwdLayout coo_bwd_layout(int64_t n_edges, int64_t n_src, int64_t n_dst, int h
     return C;
 }
 
+std::atomic<int64_t> g_edge_grid_cap{gat::kEdgeGridDefault};
+
 }  // namespace
 
+int64_t gat::edge_grid_cap() { return g_edge_grid_cap.load(std::memory_order_relaxed); }
+
 extern "C" {
+
+int64_t gat_testing_edge_grid_cap(int64_t cap) {
+    if (cap <= 0 || cap > gat::kEdgeGridDefault) cap = gat::kEdgeGridDefault;
+    return g_edge_grid_cap.exchange(cap);
+}
+
 
 const char* gat_status_str(gat_status s) {
     switch (s) {

@@ -643,7 +643,7 @@ hipError_t launch_edge_dot(int dtype, int H, int D, const int32_t* rows, const i
         constexpr int UMAX = (8 / Gm::NV) > 1 ? (8 / Gm::NV) : 1;
         constexpr int U = UMAX * Gm::P <= kWave ? UMAX : kWave / Gm::P;
         const int64_t waves = (n_edges + U * Gm::P - 1) / (U * Gm::P);
-        hipLaunchKernelGGL((edge_dot_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, kEdgeGrid)),
+        hipLaunchKernelGGL((edge_dot_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, edge_grid_cap())),
                            dim3(kBlock), 0, stream, rows, col, n_edges, gf, static_cast<const T*>(ff), out);
     });
     if (!ok) return hipErrorInvalidValue;

@@ -185,7 +185,10 @@ constexpr int64_t kSegmentGrid = 65536;
 // 2^29 edges at 16 edges per step, a grid-stride loop beyond (2^23 workgroups x 256 work-items
 // keeps the dispatch's 32-bit work-item count in range).  At 2^26 edges a grid of 65536
 // workgroups looping over the edges took 7.09 ms against 6.77 ms.
-constexpr int64_t kEdgeGrid = int64_t(1) << 23;
+constexpr int64_t kEdgeGridDefault = int64_t(1) << 23;
+// The cap in force: kEdgeGridDefault unless gat_testing_edge_grid_cap lowered it (tests use that to
+// run the grid-stride loop at sizes they can check).  Host only.
+int64_t edge_grid_cap();
 
 // kOverflow: 1 when the row degrees sum past the capacities the host sized from n_edges (row_ptr
 // breaks its precondition row_ptr[n_rows] = n_edges); the binner then leaves every table empty.

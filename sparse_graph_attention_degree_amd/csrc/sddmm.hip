@@ -91,7 +91,7 @@ hipError_t launch_sddmm(int dtype, int H, int D, const int32_t* src_idx, const i
         constexpr int UMAX = (8 / Gm::NV) > 1 ? (8 / Gm::NV) : 1;
         constexpr int U = UMAX * Gm::P <= kWave ? UMAX : kWave / Gm::P;
         const int64_t waves = (n_edges + U * Gm::P - 1) / (U * Gm::P);
-        hipLaunchKernelGGL((sddmm_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, kEdgeGrid)),
+        hipLaunchKernelGGL((sddmm_kernel<T, Tag::H, Tag::D>), dim3(grid_for(waves, kWavesPerBlock, edge_grid_cap())),
                            dim3(kBlock), 0, stream, src_idx, dst_idx, n_edges, static_cast<const T*>(src_feat),
                            static_cast<const T*>(dst_feat), scale, out);
     });

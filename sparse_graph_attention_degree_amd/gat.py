@@ -30,7 +30,7 @@ EXPORTED = ["gat_plan_workspace_bytes", "gat_plan_build", "gat_sddmm", "gat_edge
             "gat_aggregate_backward", "gat_layer_backward_workspace_bytes", "gat_fused_layer_backward",
             "gat_batch_csr", "gat_relation_block_lds_bytes", "gat_relation_block", "gat_linear",
             "gat_fused_layer_noalloc", "gat_fused_layer_noalloc_bytes", "gat_sddmm_backward_workspace_bytes",
-            "gat_sddmm_backward"]
+            "gat_sddmm_backward", "gat_testing_edge_grid_cap"]
 
 
 class GatError(RuntimeError):
@@ -97,6 +97,8 @@ def _lib():
     L.gat_sddmm_backward_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.gat_sddmm_backward_workspace_bytes.restype = sz
     L.gat_sddmm_backward.argtypes = [vp, vp, i64, vp, i64, vp, i64, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.gat_testing_edge_grid_cap.argtypes = [i64]
+    L.gat_testing_edge_grid_cap.restype = i64
     L.gat_batch_csr.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     L.gat_relation_block_lds_bytes.argtypes = [i32, i32, i32, i32]
     L.gat_relation_block_lds_bytes.restype = sz
