@@ -181,23 +181,30 @@ __global__ __launch_bounds__(kLinThreads, 2) void linear_kernel(const XT* __rest
 
 // ------------------------------------------------------------------ stationary weights, K <= 256
 // For in_dim <= 256 a wave keeps its w fragments for the whole of K in registers (2 column
-// tiles x 16 k-steps = 128 VGPRs), so w is read once per workgroup and only x streams.  A
+// tiles x 16 k-steps = 128 AGPRs), so w is read once per workgroup and only x streams.  A
 // 256-thread workgroup owns 256 output columns (one column group of 64 per wave, each wave
-// covering all rows of a block as 32-row MFMA tiles) and walks a strided stream of row blocks
-// of x (64 rows of bf16 x, 32 of fp32 x): blocks i + 1 and i + 2 wait in registers while block
-// i, in LDS, feeds the MFMAs (each 16-byte fragment of x read from LDS feeds two MFMAs); then
-// block i + 1 goes to the other LDS buffer and block i + 3 is fetched into its registers.
+// covering the 32 rows of a block as one MFMA row tile) and walks a strided stream of 32-row
+// blocks of x: blocks i + 1 and i + 2 wait in registers while block i, in LDS, feeds the MFMAs
+// (each 16-byte fragment of x read from LDS feeds two MFMAs); then block i + 1 goes to the other
+// LDS buffer and block i + 3 is fetched into its registers.  With bf16 x two workgroups share a
+// CU (244 registers per lane, 51 KB of LDS each), so that one's epilogue and barriers overlap the
+// other's MFMAs; 64-row blocks at one workgroup per CU ran the two phases back to back.
 // Vector-memory waits count in issue order, so each fetch precedes the block's stores and the
 // number of loads and stores per block is fixed (buffer accesses, no branches): waiting for a
 // fetched block then leaves every later access in flight.  The results leave through a row-major
-// LDS stage as whole 16-byte pieces of rows.  The grid holds one
-// workgroup per CU; the column blocks of one row stream are consecutive after the XCD remap, so
+// LDS stage as whole 16-byte pieces of rows, with non-temporal stores.  The grid holds one or two
+// workgroups per CU; the column blocks of one row stream are consecutive after the XCD remap, so
 // the q, k and v workgroups of the same rows share one XCD's L2 copy of x.
 constexpr int kWsK = 256;                  // largest in_dim of this path
 constexpr int kWsKK = kWsK / 16;           // MFMA k-steps
-// rows per block: 64 for bf16 x, 32 for fp32 x (whose staging registers are twice as many)
+// rows per block: one 32-row MFMA tile, for bf16 and fp32 x
 template <bool XF32>
-constexpr int ws_rows() { return XF32 ? 32 : 64; }
+constexpr int ws_rows() { return 32; }
+// Resident workgroups per CU: two where the registers allow (bf16 x, buffer stores: 244 of the
+// 256 registers a lane may hold at two waves per SIMD), so that one workgroup's epilogue and
+// barriers overlap the other's MFMAs; one otherwise.
+template <bool XF32, bool BUF>
+constexpr int ws_per_cu() { return !XF32 && BUF ? 2 : 1; }
 constexpr int kWsCols = 256;               // columns per workgroup
 constexpr int kWsThreads = 256;            // 4 column groups of 64
 constexpr int kWsPitch = kWsK + 8;         // bf16 per LDS row (528 bytes: rows 4 banks apart)
@@ -208,6 +215,7 @@ typedef unsigned int lin_u32x4 __attribute__((ext_vector_type(4)));
 // block: a byte offset at or past the size reads 0 and drops a write, so edge rows and columns
 // need no branches.
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int kStoreNt = 2;                // cache-policy bit of a non-temporal store (gfx950)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t lin_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
@@ -221,17 +229,17 @@ __device__ __forceinline__ uint4 lin_load16(__amdgpu_buffer_rsrc_t rs, uint32_t 
 template <bool XF32>
 struct RowBlock;
 
-// 64 rows x 256 bf16 = 2048 pieces of 16 bytes, eight per thread (32 threads per row)
+// 32 rows x 256 bf16 = 1024 pieces of 16 bytes, four per thread (32 threads per row)
 template <>
 struct RowBlock<false> {
-    uint4 v[8];
+    uint4 v[4];
     __device__ __forceinline__ void fetch(const void* xv, int64_t M, int K, int64_t r0, int t) {
-        const int64_t rows = r0 >= M ? 0 : M - r0 < 64 ? M - r0 : 64;
+        const int64_t rows = r0 >= M ? 0 : M - r0 < 32 ? M - r0 : 32;
         const auto rs = lin_rsrc(static_cast<const uint16_t*>(xv) + (rows > 0 ? r0 * K : 0),
                                  static_cast<uint32_t>(rows * K * 2));
         const int c = (t & 31) * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const uint32_t off = c < K ? static_cast<uint32_t>((((t >> 5) + 8 * i) * K + c) * 2) : kOob;
             v[i] = lin_load16(rs, off);
         }
@@ -239,7 +247,7 @@ struct RowBlock<false> {
     __device__ __forceinline__ void store(uint16_t* lds, int t) const {
         const int c = (t & 31) * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + ((t >> 5) + 8 * i) * kWsPitch + c) = v[i];
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + ((t >> 5) + 8 * i) * kWsPitch + c) = v[i];
     }
 };
 
@@ -270,7 +278,7 @@ struct RowBlock<true> {
 };
 
 template <bool XF32, bool Y_BF16, bool BUF>
-__global__ __launch_bounds__(kWsThreads, 1) void linear_wstat_kernel(const void* __restrict__ x,
+__global__ __launch_bounds__(kWsThreads, (ws_per_cu<XF32, BUF>())) void linear_wstat_kernel(const void* __restrict__ x,
                                                                      const uint16_t* __restrict__ w,
                                                                      const float* __restrict__ bias, int64_t M,
                                                                      int K, int N, LinearOut out, int n_col_blocks,
@@ -352,31 +360,31 @@ __global__ __launch_bounds__(kWsThreads, 1) void linear_wstat_kernel(const void*
 
     const int cl0 = wave * 64 + 4 * (lane >> 5);     // block-local column of this lane's first quad
     const int width = out.width;
-    float bq[2][16];                                  // bias of accumulator register r of tile j
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 b4 = *reinterpret_cast<const float4*>(&bs[cl0 + 32 * j + 8 * q]);
-            bq[j][4 * q] = b4.x;
-            bq[j][4 * q + 1] = b4.y;
-            bq[j][4 * q + 2] = b4.z;
-            bq[j][4 * q + 3] = b4.w;
-        }
     // one block: compute from xcur, move the next block from rbc to xnext, refill rbc three
     // blocks ahead, store the results; false after the stream's last block
     auto step = [&](RowBlock<XF32>& rbc, const uint16_t* xcur, uint16_t* xnext) -> bool {
         lin_f32x16 acc[kTi][2];                      // start from the bias: y = b + sum_k x w
 #pragma unroll
-        for (int i = 0; i < kTi; ++i)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int q = 0; q < 4; ++q) {
+                // accumulator register 4 q + e of tile j holds column cl0 + 32 j + 8 q + e
+                const float4 b4 = *reinterpret_cast<const float4*>(&bs[cl0 + 32 * j + 8 * q]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = bq[j][r];
+                for (int i = 0; i < kTi; ++i) {
+                    acc[i][j][4 * q] = b4.x;
+                    acc[i][j][4 * q + 1] = b4.y;
+                    acc[i][j][4 * q + 2] = b4.z;
+                    acc[i][j][4 * q + 3] = b4.w;
+                }
+            }
         const uint16_t* arow = &xcur[fr * kWsPitch + fk];
         lin_bf16x8 a[2][kTi];                        // fragments of step kk (kk & 1) and kk + 1
 #pragma unroll
         for (int i = 0; i < kTi; ++i) a[0][i] = *reinterpret_cast<const lin_bf16x8*>(arow + 32 * i * kWsPitch);
+        // raised issue priority while the MFMAs go out: the other workgroup's epilogue on this
+        // SIMD fills the gaps instead of delaying them
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int c = kk & 1;
@@ -391,6 +399,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void linear_wstat_kernel(const void*
                 acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][kk], a[c][i], acc[i][1], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         const int64_t nxt = blk + n_streams;
         const bool more = nxt < n_row_blocks;
         if (more) rbc.store(xnext, t);
@@ -436,34 +445,35 @@ __global__ __launch_bounds__(kWsThreads, 1) void linear_wstat_kernel(const void*
                     const int rl = t / kPiecesPerRow + kRowsPerPass * u;
                     const uint32_t off = c + kEpp <= N ? static_cast<uint32_t>((rl * width + cc) * kYB) : kOob;
                     const uint4 v = *reinterpret_cast<const uint4*>(ostage + rl * kOsPitch + cl * kYB);
+                    // non-temporal: the outputs are not read again by this kernel
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(gat_v4i, (lin_u32x4){v.x, v.y, v.z, v.w}),
-                                                           rs, off, 0, 0);
+                                                           rs, off, 0, kStoreNt);
                 }
             } else {
 #pragma unroll
-            for (int u = 0; u < kRows / kRowsPerPass; ++u) {
-                const int rl = t / kPiecesPerRow + kRowsPerPass * u;
-                const int64_t row = blk * kRows + rl;
-                if (row >= M || c >= N) continue;
-                const char* src = ostage + rl * kOsPitch + cl * kYB;
-                if (vec && c + kEpp <= N) {
-                    const int seg = (c >= width) + (c >= 2 * width);
-                    char* p = static_cast<char*>(seg == 0 ? out.p[0] : (seg == 1 ? out.p[1] : out.p[2]));
-                    *reinterpret_cast<uint4*>(p + (row * width + (c - seg * width)) * kYB) =
-                        *reinterpret_cast<const uint4*>(src);
-                } else {
-                    for (int e = 0; e < kEpp && c + e < N; ++e) {
-                        const int ce = c + e;
-                        const int seg = (ce >= width) + (ce >= 2 * width);
+                for (int u = 0; u < kRows / kRowsPerPass; ++u) {
+                    const int rl = t / kPiecesPerRow + kRowsPerPass * u;
+                    const int64_t row = blk * kRows + rl;
+                    if (row >= M || c >= N) continue;
+                    const char* src = ostage + rl * kOsPitch + cl * kYB;
+                    if (vec && c + kEpp <= N) {
+                        const int seg = (c >= width) + (c >= 2 * width);
                         char* p = static_cast<char*>(seg == 0 ? out.p[0] : (seg == 1 ? out.p[1] : out.p[2]));
-                        char* d = p + (row * width + (ce - seg * width)) * kYB;
-                        if (Y_BF16)
-                            *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(src + e * kYB);
-                        else
-                            *reinterpret_cast<float*>(d) = *reinterpret_cast<const float*>(src + e * kYB);
+                        *reinterpret_cast<uint4*>(p + (row * width + (c - seg * width)) * kYB) =
+                            *reinterpret_cast<const uint4*>(src);
+                    } else {
+                        for (int e = 0; e < kEpp && c + e < N; ++e) {
+                            const int ce = c + e;
+                            const int seg = (ce >= width) + (ce >= 2 * width);
+                            char* p = static_cast<char*>(seg == 0 ? out.p[0] : (seg == 1 ? out.p[1] : out.p[2]));
+                            char* d = p + (row * width + (ce - seg * width)) * kYB;
+                            if (Y_BF16)
+                                *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(src + e * kYB);
+                            else
+                                *reinterpret_cast<float*>(d) = *reinterpret_cast<const float*>(src + e * kYB);
+                        }
                     }
                 }
-            }
             }
         }
         if (!more) return false;
@@ -486,16 +496,17 @@ hipError_t launch_wstat(const void* x, const uint16_t* w, const float* bias, int
     if (e != hipSuccess) return e;
     const int n_col_blocks = (N + kWsCols - 1) / kWsCols;
     const int64_t n_row_blocks = (M + ws_rows<XF32>() - 1) / ws_rows<XF32>();
-    int64_t n_streams = cus / n_col_blocks;
-    if (n_streams < 1) n_streams = 1;
-    if (n_streams > n_row_blocks) n_streams = n_row_blocks;
-    const int64_t grid = n_streams * n_col_blocks;
     // 16-byte stores need pieces that do not straddle output arrays, and aligned arrays (1); the
     // buffer stores also need each workgroup's 256 columns inside one array (2)
     const int n_out = N / out.width;
     bool aligned = true;
     for (int s = 0; s < n_out; ++s) aligned = aligned && reinterpret_cast<uintptr_t>(out.p[s]) % 16 == 0;
     const int vec = !aligned ? 0 : out.width % kWsCols == 0 ? 2 : out.width % (Y_BF16 ? 8 : 4) == 0 ? 1 : 0;
+    const int per_cu = vec == 2 ? ws_per_cu<XF32, true>() : ws_per_cu<XF32, false>();
+    int64_t n_streams = (int64_t)per_cu * cus / n_col_blocks;
+    if (n_streams < 1) n_streams = 1;
+    if (n_streams > n_row_blocks) n_streams = n_row_blocks;
+    const int64_t grid = n_streams * n_col_blocks;
     if (vec == 2)
         hipLaunchKernelGGL((linear_wstat_kernel<XF32, Y_BF16, true>), dim3(static_cast<uint32_t>(grid)),
                            dim3(kWsThreads), 0, stream, x, w, bias, M, K, N, out, n_col_blocks, n_streams,

@@ -49,6 +49,7 @@ struct Engine {
     static constexpr int CM = (SC + G - 1) / G;     // column-id loads per lane per chunk
     static constexpr int UMAX = (8 * SM / NV) > 1 ? (8 * SM / NV) : 1;
     static constexpr int U = SC < UMAX ? SC : UMAX;   // gathers in flight per lane per piece
+    static constexpr int UL = U;                       // kLayer: edges per group (a k and a v row each)
 
     float acc[NV][EPP];
     float m_s, z_s;            // kSoftAgg: running max / partial sum, score layout (lane q: head q % H)
@@ -227,14 +228,14 @@ struct Engine {
         }
         if (qn != nullptr) load_q_raw(qn, qraw_n);
 #pragma unroll
-        for (int jb = 0; jb < SC; jb += U) {
+        for (int jb = 0; jb < SC; jb += UL) {
             if (!__any(jb < n)) break;
-            int cj[U];
+            int cj[UL];
 #pragma unroll
-            for (int u = 0; u < U; ++u) cj[u] = reinterpret_cast<const int*>(stage)[H * SC + jb + u];
-            uint4 kx[U][NV], vx[U][NV];
+            for (int u = 0; u < UL; ++u) cj[u] = reinterpret_cast<const int*>(stage)[H * SC + jb + u];
+            uint4 kx[UL][NV], vx[UL][NV];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UL; ++u) {
                 if (u == 0 || __any(jb + u < n)) {
 #pragma unroll
                     for (int v = 0; v < NV; ++v) {
@@ -243,9 +244,9 @@ struct Engine {
                     }
                 }
             }
-            float s[U][NV];
+            float s[UL][NV];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UL; ++u) {
                 const bool live = u == 0 || __any(jb + u < n);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
@@ -265,14 +266,14 @@ struct Engine {
             for (int v = 0; v < NV; ++v) {
                 float mx = s[0][v];
 #pragma unroll
-                for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][v]);
+                for (int u = 1; u < UL; ++u) mx = fmaxf(mx, s[u][v]);
                 const float mn = fmaxf(m_p[v], mx);
                 const float corr = exp_fast(m_p[v] - mn);
                 m_p[v] = mn;
                 z_p[v] *= corr;
                 scale_acc(v, corr);
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < UL; ++u) {
                     if (u == 0 || __any(jb + u < n)) {
                         const float pw = exp_fast(s[u][v] - mn);
                         z_p[v] += pw;
