@@ -272,9 +272,10 @@ def bench_relation(args, gat, G):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"relation block: {B} x {N} nodes, {D} features, {H} heads, {P} pair features",
                    "batch": B, "seed": args.seed},
-        "roofline": {"bound": "alu", "achieved": flops / tk / 1e12, "peak": 157.3, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": flops / tk / 1e12, "peak": 157.3, "unit": "TFLOP/s",
                      "frac": flops / tk / 1e12 / 157.3, "traffic": None,
-                     "kernel": "relation_block_kernel (one workgroup per element; fp32 vector FMA)"},
+                     "kernel": "relation_block_mfma_kernel (one workgroup per element; projections and pair "
+                               "MLP on fp32 MFMA 16x16x4, attention on the vector units)"},
         "cpu_baseline": cpu,
         "extra": {"t_call_us": tk * 1e6, "flops_per_call": flops, "hbm_bytes_per_call": nbytes,
                   "hbm_gbs": nbytes / tk / 1e9},

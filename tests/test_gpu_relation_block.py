@@ -32,11 +32,33 @@ def test_page_shapes(mask):
         assert np.array_equal(got[empty], nodes[empty])
 
 
+# (batch, nodes, dim, heads, pair_dim).  pair_dim 16 with dim a multiple of 16 up to 128 and up to 64
+# nodes runs the matrix-core kernel; the other shapes the general one.
 @pytest.mark.parametrize("shape", [(2, 7, 32, 2, 8), (1, 1, 16, 1, 4), (3, 33, 64, 8, 5), (2, 40, 128, 8, 16),
-                                   (1, 17, 48, 16, 3), (256, 24, 96, 4, 16)], ids=str)
+                                   (1, 17, 48, 16, 3), (256, 24, 96, 4, 16), (3, 64, 64, 2, 16),
+                                   (5, 1, 32, 1, 16), (2, 17, 48, 3, 16), (7, 33, 64, 8, 16), (2, 65, 64, 4, 16),
+                                   (2, 20, 160, 4, 16)], ids=str)
 def test_other_shapes(shape):
     got, want, _, _ = _run(*shape, 52, "random")
     assert_close(got, want, "f32", f"relation block {shape}")
+
+
+@pytest.mark.parametrize("mask", ["ones", "random_empty"])
+def test_misaligned_pair_features_take_the_general_kernel(mask):
+    """pair_feats (not required to be 16-byte aligned) one float past an aligned address: the
+    matrix-core kernel's 16-byte loads do not apply, the general kernel gives the same result."""
+    B, N, D, H, P = PAGE["B"], PAGE["N"], PAGE["D"], PAGE["H"], PAGE["P"]
+    nodes, pair, m, prm = G.make_relation_block(B, N, D, H, P, 54, mask=mask)
+    flat = torch.empty(pair.size + 1, dtype=torch.float32, device="cuda")
+    shifted = flat[1:].view(pair.shape)
+    shifted.copy_(torch.from_numpy(pair).cuda())
+    assert shifted.data_ptr() % 16 != 0
+    params = {k: to_dev(v) for k, v in prm.items()}
+    got = to_np(gat.gat_relation_block(to_dev(nodes), shifted, to_dev(m), params))
+    want = oracle.get().relation_attention(nodes, pair, m, prm)
+    assert_close(got, want, "f32", f"relation block, misaligned pair features ({mask})")
+    aligned = to_np(gat.gat_relation_block(to_dev(nodes), to_dev(pair), to_dev(m), params))
+    assert_close(aligned, want, "f32", f"relation block, aligned ({mask})")
 
 
 def test_in_place():
