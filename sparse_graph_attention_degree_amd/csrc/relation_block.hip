@@ -131,8 +131,8 @@ __device__ void rb_layernorm(float* xn, int N, int D, const float* __restrict__ 
 // Steps 4-6 on q, k, v [N][ld] and the biased logits lg [H][N][N] (-inf where masked): scaled q.k
 // added to the bias (lanes along j: k rows padded to ld = D + 1 land in different banks), the
 // softmax per (h, i) (a row with every pair masked becomes all zeros), and o = a v into o [N][D].
-__device__ void rb_attend(const float* qs, const float* ks, const float* vs, int ld, float* lg, int N, int D,
-                          int H, float* o) {
+__device__ void rb_attend(const float* qs, const float* ks, const float* vs, int ld, int ldv, float* lg, int N,
+                          int D, int H, float* o) {
     const int t = threadIdx.x, hd = D / H;
     const float scale = 1.f / sqrtf((float)hd);
     for (int e = t; e < H * N * N; e += kBlock) {
@@ -169,7 +169,7 @@ __device__ void rb_attend(const float* qs, const float* ks, const float* vs, int
         const float* a = lg + (h * N + i) * N;
         float s = 0.f;
 #pragma unroll 8
-        for (int j = 0; j < N; ++j) s = fmaf(a[j], vs[j * ld + c], s);
+        for (int j = 0; j < N; ++j) s = fmaf(a[j], vs[j * ldv + c], s);
         o[e] = s;
     }
     __syncthreads();
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void relation_block_kernel(
 
     // 4-6. logits, softmax, o = a v (over xn, no longer needed)
     float* o = xn;
-    rb_attend(qs, ks, vs, ld, lg, N, D, H, o);
+    rb_attend(qs, ks, vs, ld, ld, lg, N, D, H, o);
 
     // 7. out = x + o Wo^T  (projected into q's buffer, then the residual at the store)
     rb_project(o, N, D, wo, D, qs, ld, wbuf);
@@ -293,49 +293,54 @@ __device__ __forceinline__ rb_f32x4 rb_mfma(float a, float b, rb_f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// LDS of the matrix-core kernel (floats): three row arrays and the logits, 37 KB at the page's shape,
+// so four workgroups share a CU.  xn [N][D] holds x, then LayerNorm(x), then v; qs [N][D+1] holds q,
+// then o (row pitch D); ks [N][D+1] holds k, then o Wo^T.
 struct RbFastLayout {
-    int xn, qs, ks, vs, lg, mk, mb, total;
+    int xn, qs, ks, lg, mb, total;
 };
 
 __host__ __device__ inline RbFastLayout rb_fast_layout(int N, int D, int H) {
     auto up = [](int v) { return (v + 3) & ~3; };
     RbFastLayout L{};
     int o = 0;
-    L.xn = o, o += up((N + 15) / 16 * 16 * D);   // whole 16-row tiles; rows past N stay zero
+    L.xn = o, o += up(N * D);
     L.qs = o, o += up(N * (D + 1));
     L.ks = o, o += up(N * (D + 1));
-    L.vs = o, o += up(N * (D + 1));
     L.lg = o, o += up(H * N * N);
-    L.mk = o, o += up(N * N);
     L.mb = o, o += up(kRbFastP + H);            // b1, b2
     L.total = o;
     return L;
 }
 
 // One 16x16 tile of y = a w^T over KB blocks of 16 k (k past D reads 0).
+// One 16x16 tile of y = a w^T over KB blocks of 16 k: a [N][lda] in LDS, w [D][D] in global memory;
+// k past D and rows past N read 0.  The w fragments of a tile are loaded first (one L2 round trip),
+// the a fragments from LDS as each block is reached.
 template <int KB>
-__device__ __forceinline__ void rb_tile_loads(const float* a, const float* __restrict__ w, int D, int rt, int ct,
-                                              float4 (&av)[KB], float4 (&wv)[KB]) {
+__device__ __forceinline__ void rb_tile_wload(const float* __restrict__ w, int D, int ct, float4 (&wv)[KB]) {
     const int lane = lane_id(), li = lane % 16, lk = 4 * (lane / 16);
-    const float* ar = a + (rt * 16 + li) * D + lk;
     const float* wr = w + (int64_t)(ct * 16 + li) * D + lk;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        const bool in = 16 * kb + lk < D;
-        wv[kb] = in ? *reinterpret_cast<const float4*>(wr + 16 * kb) : make_float4(0.f, 0.f, 0.f, 0.f);
-        av[kb] = in ? *reinterpret_cast<const float4*>(ar + 16 * kb) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int kb = 0; kb < KB; ++kb)
+        wv[kb] = 16 * kb + lk < D ? *reinterpret_cast<const float4*>(wr + 16 * kb) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 template <int KB>
-__device__ __forceinline__ rb_f32x4 rb_tile_mfma(const float4 (&av)[KB], const float4 (&wv)[KB]) {
+__device__ __forceinline__ rb_f32x4 rb_tile_mfma(const float* a, int lda, int N, int D, int rt,
+                                                 const float4 (&wv)[KB]) {
+    const int lane = lane_id(), li = lane % 16, lk = 4 * (lane / 16);
+    const int row = rt * 16 + li;
+    const float* ar = a + row * lda + lk;
     rb_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-        acc = rb_mfma(av[kb].x, wv[kb].x, acc);
-        acc = rb_mfma(av[kb].y, wv[kb].y, acc);
-        acc = rb_mfma(av[kb].z, wv[kb].z, acc);
-        acc = rb_mfma(av[kb].w, wv[kb].w, acc);
+        const float4 av = row < N && 16 * kb + lk < D ? *reinterpret_cast<const float4*>(ar + 16 * kb)
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        acc = rb_mfma(av.x, wv[kb].x, acc);
+        acc = rb_mfma(av.y, wv[kb].y, acc);
+        acc = rb_mfma(av.z, wv[kb].z, acc);
+        acc = rb_mfma(av.w, wv[kb].w, acc);
     }
     return acc;
 }
@@ -349,25 +354,55 @@ __device__ __forceinline__ void rb_tile_store(rb_f32x4 acc, int rt, int ct, int 
     }
 }
 
-// y[i, j] = sum_k a[i, k] w[j, k], i < N, j < D: a LDS [16-row tiles][D], w global [D][D] (row-major,
-// [out, in]), y LDS with row pitch ldy.  A wave takes tiles wave, wave + 4, ... two at a time, with
-// both tiles' loads issued before the first MFMA.
+// y[i, j] = sum_k a[i, k] w[j, k], i < N, j < D: a LDS [N][lda], w global [D][D] (row-major,
+// [out, in]), y LDS with row pitch ldy (y must not overlap a).  A wave takes tiles wave, wave + 4, ...
+// two at a time, with both tiles' w loads issued before the first MFMA.
 template <int KB>
-__device__ void rb_mfma_project(const float* a, const float* __restrict__ w, int N, int D, float* y, int ldy) {
+__device__ void rb_mfma_project(const float* a, int lda, const float* __restrict__ w, int N, int D, float* y,
+                                int ldy) {
     const int wave = threadIdx.x / kWave;
     const int RT = (N + 15) / 16, CT = D / 16, T = RT * CT;
     for (int t0 = wave; t0 < T; t0 += 2 * kWavesPerBlock) {
         const int t1 = t0 + kWavesPerBlock;
-        float4 av0[KB], wv0[KB], av1[KB], wv1[KB];
-        rb_tile_loads<KB>(a, w, D, t0 / CT, t0 % CT, av0, wv0);
-        if (t1 < T) rb_tile_loads<KB>(a, w, D, t1 / CT, t1 % CT, av1, wv1);
-        rb_tile_store(rb_tile_mfma<KB>(av0, wv0), t0 / CT, t0 % CT, N, y, ldy);
-        if (t1 < T) rb_tile_store(rb_tile_mfma<KB>(av1, wv1), t1 / CT, t1 % CT, N, y, ldy);
+        float4 wv0[KB], wv1[KB];
+        rb_tile_wload<KB>(w, D, t0 % CT, wv0);
+        if (t1 < T) rb_tile_wload<KB>(w, D, t1 % CT, wv1);
+        rb_tile_store(rb_tile_mfma<KB>(a, lda, N, D, t0 / CT, wv0), t0 / CT, t0 % CT, N, y, ldy);
+        if (t1 < T) rb_tile_store(rb_tile_mfma<KB>(a, lda, N, D, t1 / CT, wv1), t1 / CT, t1 % CT, N, y, ldy);
+    }
+}
+
+// The same product written over a itself (y = a, row pitch lda): every tile is computed into
+// registers first, then after a workgroup barrier -- every wave's reads of a done -- written.  All
+// threads must call it.
+template <int KB>
+__device__ void rb_mfma_project_in_place(float* a, int lda, const float* __restrict__ w, int N, int D) {
+    // at most (kRbFastMaxN / 16) row tiles x KB column tiles over the four waves
+    constexpr int kRbMaxTilesPerWave = (kRbFastMaxN / 16) * KB / kWavesPerBlock;
+    const int wave = threadIdx.x / kWave;
+    const int RT = (N + 15) / 16, CT = D / 16, T = RT * CT;
+    rb_f32x4 acc[kRbMaxTilesPerWave];
+#pragma unroll
+    for (int u = 0; u < kRbMaxTilesPerWave; u += 2) {
+        const int t0 = wave + u * kWavesPerBlock, t1 = t0 + kWavesPerBlock;
+        if (t0 >= T) break;
+        float4 wv0[KB], wv1[KB];
+        rb_tile_wload<KB>(w, D, t0 % CT, wv0);
+        if (t1 < T) rb_tile_wload<KB>(w, D, t1 % CT, wv1);
+        acc[u] = rb_tile_mfma<KB>(a, lda, N, D, t0 / CT, wv0);
+        if (t1 < T) acc[u + 1] = rb_tile_mfma<KB>(a, lda, N, D, t1 / CT, wv1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRbMaxTilesPerWave; ++u) {
+        const int tt = wave + u * kWavesPerBlock;
+        if (tt >= T) break;
+        rb_tile_store(acc[u], tt / CT, tt % CT, N, a, lda);
     }
 }
 
 template <int KB>
-__global__ __launch_bounds__(kBlock) void relation_block_mfma_kernel(
+__global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
     const float* nodes, const float* __restrict__ pair, const float* __restrict__ mask,
     const float* __restrict__ gamma, const float* __restrict__ beta, float eps, const float* __restrict__ wq,
     const float* __restrict__ wk, const float* __restrict__ wv, const float* __restrict__ wo,
@@ -379,21 +414,16 @@ __global__ __launch_bounds__(kBlock) void relation_block_mfma_kernel(
     const int li = lane % 16, lk = 4 * (lane / 16);
     const int ND = N * D, NN = N * N, ld = D + 1;
     const RbFastLayout L = rb_fast_layout(N, D, H);
-    float* xn = lds + L.xn;          // [16-row tiles][D]: x, LayerNorm(x), then o; rows past N zero
-    float* qs = lds + L.qs;          // [N][ld]
-    float* ks = lds + L.ks;
-    float* vs = lds + L.vs;
+    float* xn = lds + L.xn;          // [N][D]: x, LayerNorm(x), then v
+    float* qs = lds + L.qs;          // [N][ld]: q, then o (pitch D)
+    float* ks = lds + L.ks;          // [N][ld]: k, then o Wo^T
     float* lg = lds + L.lg;          // [H][N][N]
-    float* mk = lds + L.mk;          // [N][N]
     float* mb = lds + L.mb;          // b1 [16], b2 [H]
     const float* x = nodes + (int64_t)b * ND;
 
-    // 0. x (and zero padding rows), the mask, the MLP biases into LDS
+    // 0. x and the MLP biases into LDS
     for (int e = t; e < ND / 4; e += kBlock)
         reinterpret_cast<float4*>(xn)[e] = reinterpret_cast<const float4*>(x)[e];
-    for (int e = ND + t; e < (N + 15) / 16 * 16 * D; e += kBlock) xn[e] = 0.f;
-    const float* mg = mask + (int64_t)b * NN;
-    for (int e = t; e < NN; e += kBlock) mk[e] = mg[e];
     if (t < kRbFastP) mb[t] = b1[t];
     if (t < H) mb[kRbFastP + t] = b2[t];
     __syncthreads();
@@ -404,9 +434,10 @@ __global__ __launch_bounds__(kBlock) void relation_block_mfma_kernel(
         const float4 w2f = li < H ? *reinterpret_cast<const float4*>(w2 + li * kRbFastP + lk)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
         const float* fp = pair + (int64_t)b * NN * kRbFastP;
+        const float* mg = mask + (int64_t)b * NN;
         const int PT = (NN + 15) / 16;
-        // pairs pt*16 .. +15 with the features f of pair pt*16 + li (k = lk .. lk + 3)
-        auto tile = [&](int pt, const float4& f) {
+        // pairs pt*16 .. +15 with the features f of pair pt*16 + li (k = lk .. lk + 3) and its mask
+        auto tile = [&](int pt, const float4& f, float keepv) {
             const int p = pt * 16 + li;
             rb_f32x4 h = {0.f, 0.f, 0.f, 0.f};
             h = rb_mfma(w1f.x, f.x, h);
@@ -425,7 +456,7 @@ __global__ __launch_bounds__(kBlock) void relation_block_mfma_kernel(
             c = rb_mfma(w2f.z, sl[2], c);
             c = rb_mfma(w2f.w, sl[3], c);
             if (p < NN) {
-                const bool keep = mk[p] >= 0.5f;
+                const bool keep = keepv >= 0.5f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int h2 = lk + r;
@@ -433,40 +464,42 @@ __global__ __launch_bounds__(kBlock) void relation_block_mfma_kernel(
                 }
             }
         };
-        // the features of kRbPairBatch tiles are loaded together, then consumed: one memory latency
-        // per batch instead of one per tile
+        // the features and mask entries of kRbPairBatch tiles are loaded together, then consumed: one
+        // memory latency per batch instead of one per tile
         for (int pt0 = wave; pt0 < PT; pt0 += kRbPairBatch * kWavesPerBlock) {
             float4 fb[kRbPairBatch];
+            float kb[kRbPairBatch];
 #pragma unroll
             for (int u = 0; u < kRbPairBatch; ++u) {
                 const int p = (pt0 + u * kWavesPerBlock) * 16 + li;
                 fb[u] = p < NN ? *reinterpret_cast<const float4*>(fp + (int64_t)p * kRbFastP + lk)
                                : make_float4(0.f, 0.f, 0.f, 0.f);
+                kb[u] = p < NN ? mg[p] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < kRbPairBatch; ++u)
-                if (pt0 + u * kWavesPerBlock < PT) tile(pt0 + u * kWavesPerBlock, fb[u]);
+                if (pt0 + u * kWavesPerBlock < PT) tile(pt0 + u * kWavesPerBlock, fb[u], kb[u]);
         }
     }
 
-    // 2. LayerNorm in place (rows < N)
+    // 2. LayerNorm in place
     rb_layernorm(xn, N, D, gamma, beta, eps);
     __syncthreads();
 
-    // 3. q, k, v
-    rb_mfma_project<KB>(xn, wq, N, D, qs, ld);
-    rb_mfma_project<KB>(xn, wk, N, D, ks, ld);
-    rb_mfma_project<KB>(xn, wv, N, D, vs, ld);
+    // 3. q, k into their buffers, then v over LayerNorm(x) (all reads of xn before the writes)
+    rb_mfma_project<KB>(xn, D, wq, N, D, qs, ld);
+    rb_mfma_project<KB>(xn, D, wk, N, D, ks, ld);
+    rb_mfma_project_in_place<KB>(xn, D, wv, N, D);
     __syncthreads();
 
-    // 4-6. logits, softmax, o = a v into xn (padding rows stay zero)
-    rb_attend(qs, ks, vs, ld, lg, N, D, H, xn);
+    // 4-6. logits, softmax, o = a v into q's buffer (q is no longer read once the logits exist)
+    rb_attend(qs, ks, xn, ld, D, lg, N, D, H, qs);
 
-    // 7. out = x + o Wo^T (projected into q's buffer, then the residual at the store)
-    rb_mfma_project<KB>(xn, wo, N, D, qs, ld);
+    // 7. out = x + o Wo^T (projected into k's buffer, then the residual at the store)
+    rb_mfma_project<KB>(qs, D, wo, N, D, ks, ld);
     __syncthreads();
     float* ob = out + (int64_t)b * ND;
-    for (int e = t; e < ND; e += kBlock) ob[e] = x[e] + qs[(e / D) * ld + e % D];
+    for (int e = t; e < ND; e += kBlock) ob[e] = x[e] + ks[(e / D) * ld + e % D];
 }
 
 }  // namespace
