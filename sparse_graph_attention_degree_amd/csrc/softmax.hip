@@ -91,19 +91,28 @@ constexpr int kBlkRows = 32;       // rows per wave (at most: fewer on graphs to
 constexpr int64_t kSmFillWaves = 2048;
 constexpr int kBlkBudget = 1024;   // floats per group (whole rows), 16 per lane
 
-// Per-(row, head) maxima of a group combine with LDS atomic integer max on an order-preserving key
-// of the float (finite scores; -inf maps below every finite value).
-__device__ __forceinline__ int max_key(float x) {
-    const int b = __float_as_int(x);
-    return b ^ ((b >> 31) & 0x7fffffff);
-}
-__device__ __forceinline__ float key_max(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
-
-// Sums of exp(s - max) combine in 64-bit fixed point: each term, in (0, 1], is truncated to a
-// multiple of 2^-31, so the sum is exact integer arithmetic, the same in any order.  A row of
-// n edges sums to at least 2^31 (its maximum contributes exactly 1), and the truncation moves the
-// sum by less than n 2^-31 relative to that.
-constexpr float kFix = 2147483648.f;   // 2^31
+// Per-(row, head) maxima of a group combine with the LDS float max atomic (ds_max_f32: exact, so the
+// same in any order).  Sums of exp(s - max) combine in fixed point: each term, in (0, 1], is
+// truncated to a multiple of 1 / scale, so the sum is exact integer arithmetic, the same in any
+// order.  A row of n edges sums to at least scale (its maximum contributes exactly 1), and the
+// truncation moves the sum by less than n / scale relative to that.  Rows of up to kZ32Rows edges
+// use 32-bit sums with scale 2^24 (n / scale <= 7.6e-6, 128 * 2^24 = 2^31 fits); longer ones (a
+// group takes rows of up to 1024 / H edges) 64-bit sums with scale 2^31.
+constexpr int kZ32Rows = 128;
+template <bool Z32>
+struct FixSum;
+template <>
+struct FixSum<true> {
+    using type = unsigned;
+    static constexpr float scale = 16777216.f;      // 2^24
+    __device__ static type of(float p) { return (unsigned)(p * scale); }
+};
+template <>
+struct FixSum<false> {
+    using type = unsigned long long;
+    static constexpr float scale = 2147483648.f;    // 2^31
+    __device__ static type of(float p) { return (unsigned long long)(unsigned)(p * scale); }
+};
 
 // Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per rpw (<= 32) consecutive rows, in
 // groups of consecutive such rows (whole rows, at most kBlkBudget floats).  A row of another class
@@ -114,24 +123,26 @@ constexpr float kFix = 2147483648.f;   // 2^31
 // masked).  The row of each edge comes from a table of the group's row starts in LDS (the row
 // lanes mark their first edge; a max-scan over the lane's edges and over the lanes spreads the
 // marks).  Then, per (row, head): the lane folds its own edges of one row (a running value that
-// restarts where the row changes), and LDS atomics combine the lanes' parts -- an integer max of
-// order-preserving keys (exact), then the sum of exp(s - max) in 64-bit fixed point (kFix: exact
-// integer adds) -- so a row's result is the same whatever rows share its group or lane.
-// alpha = exp(s - max) * (2^31 / sum) leaves with four 16-byte buffer stores.
-template <int H>
+// restarts where the row changes), and LDS atomics combine the lanes' parts -- a float max
+// (exact), then the sum of exp(s - max) in fixed point (FixSum: exact integer adds) -- so a row's
+// result is the same whatever rows share its group or lane.  alpha = exp(s - max) * (scale / sum)
+// leaves with four 16-byte buffer stores.
+template <int H, bool Z32>
 __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __restrict__ row_ptr, int64_t n_rows,
                                                                const float* sc, float* out, int hi, int rpw) {
+    using Fix = FixSum<Z32>;
+    using ZT = typename Fix::type;
     constexpr int EPL = 16 / H;                // edges per lane
     constexpr int RIDB = kBlkBudget / H;       // edges per group, at most: bytes of the row table
     constexpr int NRH = kBlkRows * H;          // (row, head) slots
     __shared__ __align__(16) unsigned char rid_all[kWavesPerBlock][RIDB];
-    __shared__ __align__(16) int mk_all[kWavesPerBlock][NRH];            // max keys, then 2^31 / sum
-    __shared__ __align__(16) unsigned long long z_all[kWavesPerBlock][NRH];
+    __shared__ __align__(16) float mx_all[kWavesPerBlock][NRH];          // maxima, then scale / sum
+    __shared__ __align__(16) ZT z_all[kWavesPerBlock][NRH];
     const int wv = threadIdx.x / kWave;
     unsigned char* rid_t = rid_all[wv];
-    int* mk = mk_all[wv];
-    float* rzs = reinterpret_cast<float*>(mk);
-    unsigned long long* zs = z_all[wv];
+    float* mx = mx_all[wv];
+    float* rzs = mx;
+    ZT* zs = z_all[wv];
     const int lane = lane_id();
     const int64_t r0 = ((int64_t)blockIdx.x * kWavesPerBlock + wv) * rpw;
     if (r0 >= n_rows) return;
@@ -177,8 +188,8 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         // clear the row table; reset the (row, head) slots
         if (lane * 16 < RIDB) *reinterpret_cast<uint4*>(rid_t + lane * 16) = make_uint4(0, 0, 0, 0);
         for (int t = lane; t < nrows * H; t += kWave) {
-            mk[t] = max_key(-INFINITY);
-            zs[t] = 0ull;
+            mx[t] = -INFINITY;
+            zs[t] = 0;
         }
         wave_lds_handoff();
         if (lane >= i && lane < j && deg > 0) rid_t[rb - base] = (unsigned char)(lane - i + 1);
@@ -237,14 +248,14 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 for (int h = 0; h < H; ++h) {
                     const float v = x[k * H + h];
                     run[h] = restart ? v : fmaxf(run[h], v);
-                    if (valid && lastk) atomicMax(&mk[rid[k] * H + h], max_key(run[h]));
+                    if (valid && lastk) atomicMax(&mx[rid[k] * H + h], run[h]);
                 }
             }
         }
         wave_lds_handoff();
         // exp(s - max); its fixed-point sum per (row, head), folded the same way, then atomics
         {
-            unsigned long long run[H];
+            ZT run[H];
 #pragma unroll
             for (int k = 0; k < EPL; ++k) {
                 const bool valid = (lane * 16 + k * H) < len;
@@ -253,16 +264,16 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 const int slot = (valid ? rid[k] : 0) * H;
 #pragma unroll
                 for (int h = 0; h < H; ++h) {
-                    const float p = valid ? exp_fast(x[k * H + h] - key_max(mk[slot + h])) : 0.f;
+                    const float p = valid ? exp_fast(x[k * H + h] - mx[slot + h]) : 0.f;
                     x[k * H + h] = p;
-                    const unsigned long long f = (unsigned long long)(unsigned)(p * kFix);
+                    const ZT f = Fix::of(p);
                     run[h] = restart ? f : run[h] + f;
                     if (valid && lastk) atomicAdd(&zs[rid[k] * H + h], run[h]);
                 }
             }
         }
         wave_lds_handoff();
-        for (int t = lane; t < nrows * H; t += kWave) rzs[t] = kFix / (float)zs[t];
+        for (int t = lane; t < nrows * H; t += kWave) rzs[t] = Fix::scale / (float)zs[t];
         wave_lds_handoff();
 #pragma unroll
         for (int k = 0; k < EPL; ++k) {
@@ -480,8 +491,12 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         int64_t rpw = (n_rows + kSmFillWaves - 1) / kSmFillWaves;   // enough waves to fill the device
         rpw = rpw < 1 ? 1 : (rpw > kBlkRows ? kBlkRows : rpw);
         const int64_t bwaves = (n_rows + rpw - 1) / rpw;
-        hipLaunchKernelGGL(softmax_block_kernel<HH>, dim3(grid_for(bwaves, kWavesPerBlock, INT32_MAX)), dim3(kBlock),
-                           0, stream, row_ptr, n_rows, scores, out, staged, (int)rpw);
+        if (staged <= kZ32Rows)
+            hipLaunchKernelGGL((softmax_block_kernel<HH, true>), dim3(grid_for(bwaves, kWavesPerBlock, INT32_MAX)),
+                               dim3(kBlock), 0, stream, row_ptr, n_rows, scores, out, staged, (int)rpw);
+        else
+            hipLaunchKernelGGL((softmax_block_kernel<HH, false>), dim3(grid_for(bwaves, kWavesPerBlock, INT32_MAX)),
+                               dim3(kBlock), 0, stream, row_ptr, n_rows, scores, out, staged, (int)rpw);
         if (short_max > staged) {
             const int64_t waves = (n_rows + kSmRowsPerWave - 1) / kSmRowsPerWave;
             hipLaunchKernelGGL(softmax_short_kernel<HH>, dim3(grid_for(waves, kWavesPerBlock, INT32_MAX)),
