@@ -167,7 +167,8 @@ constexpr uint32_t kCscMagic = 0x47415443u;   // "GATC"
 
 struct CscLayout {
     gat::RadixPlan sort;
-    size_t off_col_ptr, off_row_idx, off_rows, off_keys[2], off_vals[2], off_hist, off_sums, off_stage, off_plan;
+    size_t off_col_ptr, off_row_idx, off_rows, off_keys[2], off_vals[2], off_rows2, off_hist, off_sums, off_stage,
+        off_plan;
     Layout plan;
     size_t total;
 };
@@ -190,6 +191,7 @@ CscLayout csc_layout(int64_t n_rows, int64_t n_src, int64_t n_edges, int heads, 
         C.off_keys[b] = take((size_t)n_edges * 4);
         C.off_vals[b] = take((size_t)n_edges * 4);
     }
+    C.off_rows2 = take((size_t)n_edges * 4);   // the rows between passes (row_idx takes the last pass)
     C.off_hist = take((size_t)hist * 4);
     C.off_sums = take((size_t)(gat::scan_tiles(hist) + 1) * 4);
     C.off_stage = take((size_t)n_edges * heads * 4);
@@ -235,7 +237,7 @@ BwdLayout bwd_layout(int64_t n_edges, int heads) {
 // the CSR of the grouping and its plan, and runs the aggregation.  Both sides reuse the same
 // buffers, sized for the larger side.
 struct CooBwdLayout {
-    size_t off_row_ptr, off_col, off_keys[2], off_vals[2], off_hist, off_sums, off_w, off_plan, total;
+    size_t off_row_ptr, off_col, off_col2, off_keys[2], off_vals[2], off_hist, off_sums, off_w, off_plan, total;
     size_t plan_bytes;
 };
 
@@ -251,6 +253,7 @@ CooBwdLayout coo_bwd_layout(int64_t n_edges, int64_t n_src, int64_t n_dst, int h
     };
     C.off_row_ptr = take((size_t)(n_max + 1) * 4);
     C.off_col = take((size_t)n_edges * 4);
+    C.off_col2 = take((size_t)n_edges * 4);   // the other endpoint between passes (col takes the last)
     for (int b = 0; b < 2; ++b) {
         C.off_keys[b] = take((size_t)n_edges * 4);
         C.off_vals[b] = take((size_t)n_edges * 4);
@@ -537,16 +540,19 @@ gat_status gat_csc_build(const int32_t* row_ptr, const int32_t* col_idx, int64_t
     char* base = static_cast<char*>(ws);
     auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
     hipError_t e = gat::launch_expand_rows(row_ptr, n_rows, I(C.off_rows), stream);
-    // stable LSD passes over the column bits: (column, edge id) ends sorted by column, then edge id
-    for (int pass = 0; e == hipSuccess && pass < C.sort.passes; ++pass) {
+    // stable LSD passes over the column bits: (column, edge id) ends sorted by column, then edge id,
+    // with each edge's row carried along (the last pass writes it into row_idx)
+    const int np = C.sort.passes;
+    auto rows_out = [&](int pass) { return I((np - 1 - pass) % 2 == 0 ? C.off_row_idx : C.off_rows2); };
+    for (int pass = 0; e == hipSuccess && pass < np; ++pass) {
         const int32_t* kin = pass == 0 ? col_idx : I(C.off_keys[(pass - 1) % 2]);
         const int32_t* vin = pass == 0 ? nullptr : I(C.off_vals[(pass - 1) % 2]);
-        e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), n_edges,
-                                   pass * C.sort.bits, C.sort.bits, I(C.off_hist), I(C.off_sums), stream);
+        const int32_t* rin = pass == 0 ? I(C.off_rows) : rows_out(pass - 1);
+        e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), rin, rows_out(pass),
+                                   n_edges, pass * C.sort.bits, C.sort.bits, I(C.off_hist), I(C.off_sums), stream);
     }
     if (e == hipSuccess)
-        e = gat::launch_csc_finish(I(C.off_keys[(C.sort.passes - 1) % 2]), I(c.off_perm), I(C.off_rows), n_edges,
-                                   n_src, I(C.off_col_ptr), I(C.off_row_idx), stream);
+        e = gat::launch_bounds_from_keys(I(C.off_keys[(np - 1) % 2]), n_edges, n_src, I(C.off_col_ptr), stream);
     if (e == hipSuccess)
         e = build_plan(I(C.off_col_ptr), n_src, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN,
                        C.plan, base + C.off_plan, C.plan.total, &c.plan, stream);
@@ -716,17 +722,23 @@ gat_status gat_sddmm_backward(const int32_t* src_idx, const int32_t* dst_idx, in
         if (sd.out == nullptr || sd.n_rows == 0) continue;
         // stable LSD passes over the key bits: (key, edge id) ends sorted by key, then edge id.  With no
         // edges the passes enqueue nothing, row_ptr is all zeros and the aggregation writes +0.0 rows.
+        // (the other endpoint rides along; the last pass writes it into col)
         const gat::RadixPlan rp = gat::radix_plan(sd.n_rows);
-        for (int pass = 0; e == hipSuccess && pass < rp.passes; ++pass) {
+        const int np = rp.passes;
+        auto other_out = [&](int pass) { return I((np - 1 - pass) % 2 == 0 ? C.off_col : C.off_col2); };
+        for (int pass = 0; e == hipSuccess && pass < np; ++pass) {
             const int32_t* kin = pass == 0 ? sd.key : I(C.off_keys[(pass - 1) % 2]);
             const int32_t* vin = pass == 0 ? nullptr : I(C.off_vals[(pass - 1) % 2]);
-            e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), n_edges,
-                                       pass * rp.bits, rp.bits, I(C.off_hist), I(C.off_sums), stream);
+            const int32_t* oin = pass == 0 ? sd.other : other_out(pass - 1);
+            e = gat::launch_radix_pass(kin, vin, I(C.off_keys[pass % 2]), I(C.off_vals[pass % 2]), oin,
+                                       other_out(pass), n_edges, pass * rp.bits, rp.bits, I(C.off_hist),
+                                       I(C.off_sums), stream);
         }
-        const int32_t* perm = I(C.off_vals[(rp.passes - 1) % 2]);
+        const int32_t* perm = I(C.off_vals[(np - 1) % 2]);
         if (e == hipSuccess)
-            e = gat::launch_group_finish(heads, I(C.off_keys[(rp.passes - 1) % 2]), perm, sd.other, grad_out, scale,
-                                         n_edges, sd.n_rows, row_ptr, col, w, stream);
+            e = gat::launch_bounds_from_keys(I(C.off_keys[(np - 1) % 2]), n_edges, sd.n_rows, row_ptr, stream);
+        // the scaled gradient in the grouping's order
+        if (e == hipSuccess) e = gat::launch_permute_edges(heads, perm, grad_out, n_edges, scale, w, stream);
         gat_plan plan;
         const Layout L =
             plan_layout(sd.n_rows, n_edges, heads, head_dim, GAT_DEFAULT_SHORT_MAX, GAT_DEFAULT_SEG_LEN);

@@ -12,7 +12,8 @@
 //  * radix_hist / radix_scatter: one pass of an LSD radix sort (digits of up to 8 bits) of
 //    (column, edge id) pairs, stable, so the final order is by column and then by edge id; scan_*:
 //    the exclusive scan of the per-tile digit counts between the two.
-//  * csc_bounds: column pointers from the sorted columns; gather_rows: row id per CSC entry.
+//  * csc_bounds: column pointers from the sorted columns (the row of each CSC entry rides along
+//    through the sort as a second value).
 //  * permute_edges: per-edge values [E,H] moved into CSC order.
 //  * edge_dot: per edge and head, <G[row(e)], F[col(e)]> with G fp32 and F fp32 or bf16 (the
 //    gradient of the aggregation weights, and of the softmax output in the fused backward).
@@ -86,15 +87,22 @@ __device__ int block_exscan_int(int v, int& total);
 
 // vin == nullptr: the values are the item positions (the first pass, identity order).
 // offs[d * n_tiles + tile]: the output position of the tile's first item of digit d.
+// V2: a second value per item (v2in -> v2out) moves with the key, so that a payload known in the
+// input order (the row of a CSR edge, the other end of a COO edge) arrives sorted without a gather
+// through the permutation afterwards.
+template <bool V2>
 __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const int32_t* __restrict__ kin,
                                                                const int32_t* __restrict__ vin,
                                                                int32_t* __restrict__ kout, int32_t* __restrict__ vout,
-                                                               int64_t n, int shift, int bits,
-                                                               const int32_t* __restrict__ offs, int64_t n_tiles) {
+                                                               const int32_t* __restrict__ v2in,
+                                                               int32_t* __restrict__ v2out, int64_t n, int shift,
+                                                               int bits, const int32_t* __restrict__ offs,
+                                                               int64_t n_tiles) {
     __shared__ int wcnt[kWavesPerBlock][kRadixMaxBins];   // per wave and digit: count, then the wave's base
     __shared__ int dstart[kRadixMaxBins];                   // digit's first slot in the tile
     __shared__ int dglobal[kRadixMaxBins];                  // output position of slot 0 of the digit's run
     __shared__ int skey[kSortTile], sval[kSortTile];
+    __shared__ int sval2[V2 ? kSortTile : 1];
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     const int bins = 1 << bits, mask = bins - 1;
     const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;
@@ -103,13 +111,14 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const int32_t* __
 #pragma unroll
     for (int wv = 0; wv < kWavesPerBlock; ++wv) wcnt[wv][t] = 0;
     __syncthreads();
-    int key[kSortItems], val[kSortItems], rank[kSortItems];
+    int key[kSortItems], val[kSortItems], rank[kSortItems], val2[V2 ? kSortItems : 1];
 #pragma unroll
     for (int k = 0; k < kSortItems; ++k) {
         const int64_t i = run0 + (int64_t)k * kWave + lane;
         const bool valid = i < n;
         key[k] = valid ? kin[i] : 0;
         val[k] = valid ? (vin ? vin[i] : (int32_t)i) : 0;
+        if constexpr (V2) val2[k] = valid ? v2in[i] : 0;
     }
 #pragma unroll
     for (int k = 0; k < kSortItems; ++k) {
@@ -152,6 +161,7 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const int32_t* __
             const int slot = dstart[d] + wcnt[w][d] + rank[k];
             skey[slot] = key[k];
             sval[slot] = val[k];
+            if constexpr (V2) sval2[slot] = val2[k];
         }
     }
     __syncthreads();
@@ -161,6 +171,7 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const int32_t* __
         const int64_t pos = (int64_t)dglobal[(kk >> shift) & mask] + i;
         kout[pos] = kk;
         vout[pos] = sval[i];
+        if constexpr (V2) v2out[pos] = sval2[i];
     }
 }
 
@@ -247,13 +258,6 @@ __global__ __launch_bounds__(kBlock) void csc_bounds_kernel(const int32_t* __res
     }
 }
 
-__global__ __launch_bounds__(kBlock) void gather_rows_kernel(const int32_t* __restrict__ perm,
-                                                             const int32_t* __restrict__ rows, int64_t n,
-                                                             int32_t* __restrict__ row_idx) {
-    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n; p += (int64_t)gridDim.x * kBlock)
-        row_idx[p] = rows[perm[p]];
-}
-
 // dst[p,:] = scale * src[perm[p],:] for [E,H] per-edge values (scale 1 moves the bits unchanged)
 template <int H>
 __global__ __launch_bounds__(kBlock) void permute_edges_kernel(const int32_t* __restrict__ perm,
@@ -274,34 +278,6 @@ __global__ __launch_bounds__(kBlock) void permute_edges_kernel(const int32_t* __
         } else {
 #pragma unroll
             for (int h = 0; h < H; ++h) dst[p * H + h] = scale * src[e * H + h];
-        }
-    }
-}
-
-// The entries of an edge list grouped by one endpoint (perm: edge id per sorted position):
-// col[p] = other[perm[p]] and w[p,:] = scale * grad[perm[p],:], [E,H] fp32, in one pass over perm.
-template <int H>
-__global__ __launch_bounds__(kBlock) void gather_entries_kernel(const int32_t* __restrict__ perm,
-                                                                const int32_t* __restrict__ other,
-                                                                const float* __restrict__ grad, int64_t n,
-                                                                float scale, int32_t* __restrict__ col,
-                                                                float* __restrict__ w) {
-    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n; p += (int64_t)gridDim.x * kBlock) {
-        const int64_t e = perm[p];
-        col[p] = other[e];
-        if constexpr (H % 4 == 0) {
-#pragma unroll
-            for (int h = 0; h < H; h += 4) {
-                float4 x = *reinterpret_cast<const float4*>(grad + e * H + h);
-                x.x *= scale;
-                x.y *= scale;
-                x.z *= scale;
-                x.w *= scale;
-                *reinterpret_cast<float4*>(w + p * H + h) = x;
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < H; ++h) w[p * H + h] = scale * grad[e * H + h];
         }
     }
 }
@@ -574,16 +550,22 @@ hipError_t launch_exclusive_scan(const int32_t* in, int64_t n, int32_t* sums, in
     return hipGetLastError();
 }
 
-hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout, int64_t n,
-                             int shift, int bits, int32_t* hist, int32_t* sums, hipStream_t stream) {
+hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout,
+                             const int32_t* v2in, int32_t* v2out, int64_t n, int shift, int bits, int32_t* hist,
+                             int32_t* sums, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     if (bits < 1 || bits > kRadixMaxBits || shift < 0 || shift > 30) return hipErrorInvalidValue;
+    if ((v2in == nullptr) != (v2out == nullptr)) return hipErrorInvalidValue;
     const int64_t nt = radix_tiles(n);
     hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, n, shift, bits, hist, nt);
     const hipError_t e = launch_exclusive_scan(hist, nt << bits, sums, hist, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, vin, kout, vout, n,
-                       shift, bits, hist, nt);
+    if (v2out)
+        hipLaunchKernelGGL(radix_scatter_kernel<true>, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, vin, kout,
+                           vout, v2in, v2out, n, shift, bits, hist, nt);
+    else
+        hipLaunchKernelGGL(radix_scatter_kernel<false>, dim3((unsigned)nt), dim3(kBlock), 0, stream, kin, vin, kout,
+                           vout, v2in, v2out, n, shift, bits, hist, nt);
     return hipGetLastError();
 }
 
@@ -596,28 +578,10 @@ RadixPlan radix_plan(int64_t n_keys) {
     return p;
 }
 
-hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
-                             int64_t n_src, int32_t* col_ptr, int32_t* row_idx, hipStream_t stream) {
-    hipLaunchKernelGGL(csc_bounds_kernel, dim3(grid_for(n_edges + 1, kBlock, 65536)), dim3(kBlock), 0, stream, skeys,
-                       n_edges, n_src, col_ptr);
-    if (n_edges > 0)
-        hipLaunchKernelGGL(gather_rows_kernel, dim3(grid_for(n_edges, kBlock, 65536)), dim3(kBlock), 0, stream, perm,
-                           rows, n_edges, row_idx);
-    return hipGetLastError();
-}
-
-hipError_t launch_group_finish(int H, const int32_t* skeys, const int32_t* perm, const int32_t* other,
-                               const float* grad, float scale, int64_t n_edges, int64_t n_rows, int32_t* row_ptr,
-                               int32_t* col, float* w, hipStream_t stream) {
+hipError_t launch_bounds_from_keys(const int32_t* skeys, int64_t n_edges, int64_t n_rows, int32_t* row_ptr,
+                                   hipStream_t stream) {
     hipLaunchKernelGGL(csc_bounds_kernel, dim3(grid_for(n_edges + 1, kBlock, 65536)), dim3(kBlock), 0, stream, skeys,
                        n_edges, n_rows, row_ptr);
-    if (n_edges == 0) return hipGetLastError();
-    const bool ok = dispatch_heads(H, [&](auto tag) {
-        constexpr int HH = decltype(tag)::H;
-        hipLaunchKernelGGL(gather_entries_kernel<HH>, dim3(grid_for(n_edges, kBlock, 65536)), dim3(kBlock), 0, stream,
-                           perm, other, grad, n_edges, scale, col, w);
-    });
-    if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -119,19 +119,15 @@ struct RadixPlan {
 RadixPlan radix_plan(int64_t n_keys);
 
 // one stable pass on bits [shift, shift+bits) of the keys; vin == nullptr means values = positions.
+// v2in / v2out (both or neither): a second value carried with each key.
 // hist: int32 [256 * radix_tiles(n)], sums: int32 [scan_tiles(256 * radix_tiles(n)) + 1].
-hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout, int64_t n,
-                             int shift, int bits, int32_t* hist, int32_t* sums, hipStream_t stream);
+hipError_t launch_radix_pass(const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout,
+                             const int32_t* v2in, int32_t* v2out, int64_t n, int shift, int bits, int32_t* hist,
+                             int32_t* sums, hipStream_t stream);
 
-// col_ptr [n_src+1] from the sorted columns; row_idx[p] = rows[perm[p]]
-hipError_t launch_csc_finish(const int32_t* skeys, const int32_t* perm, const int32_t* rows, int64_t n_edges,
-                             int64_t n_src, int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
-
-// An edge list grouped by one endpoint, from the sorted keys (< n_rows) and perm of the radix passes:
-// row_ptr [n_rows+1], col[p] = other[perm[p]], w[p,:] = scale * grad[perm[p],:] ([E,H] fp32).
-hipError_t launch_group_finish(int H, const int32_t* skeys, const int32_t* perm, const int32_t* other,
-                               const float* grad, float scale, int64_t n_edges, int64_t n_rows, int32_t* row_ptr,
-                               int32_t* col, float* w, hipStream_t stream);
+// row_ptr [n_rows+1] of the grouping from the sorted keys (< n_rows)
+hipError_t launch_bounds_from_keys(const int32_t* skeys, int64_t n_edges, int64_t n_rows, int32_t* row_ptr,
+                                   hipStream_t stream);
 
 // dst[p,:] = scale * src[perm[p],:], [E,H] fp32
 hipError_t launch_permute_edges(int H, const int32_t* perm, const float* src, int64_t n, float scale, float* dst,
