@@ -128,26 +128,27 @@ __device__ void rb_layernorm(float* xn, int N, int D, const float* __restrict__ 
     }
 }
 
-// Steps 4-6 on q, k, v [N][ld] and the biased logits lg [H][N][N] (-inf where masked): scaled q.k
+// Steps 4-6 on q, k, v [N][ld] and the biased logits lg [H][N][ldl] (-inf where masked): scaled q.k
 // added to the bias (lanes along j: k rows padded to ld = D + 1 land in different banks), the
 // softmax per (h, i) (a row with every pair masked becomes all zeros), and o = a v into o [N][D].
-__device__ void rb_attend(const float* qs, const float* ks, const float* vs, int ld, int ldv, float* lg, int N,
-                          int D, int H, float* o) {
+__device__ void rb_attend(const float* qs, const float* ks, const float* vs, int ld, int ldv, float* lg, int ldl,
+                          int N, int D, int H, float* o) {
     const int t = threadIdx.x, hd = D / H;
     const float scale = 1.f / sqrtf((float)hd);
     for (int e = t; e < H * N * N; e += kBlock) {
-        if (lg[e] == -INFINITY) continue;
         const int h = e / (N * N), i = (e / N) % N, j = e % N;
+        float* l = lg + (h * N + i) * ldl + j;
+        if (*l == -INFINITY) continue;
         const float* qi = qs + i * ld + h * hd;
         const float* kj = ks + j * ld + h * hd;
         float d = 0.f;
 #pragma unroll 8
         for (int c = 0; c < hd; ++c) d = fmaf(qi[c], kj[c], d);
-        lg[e] = fmaf(d, scale, lg[e]);
+        *l = fmaf(d, scale, *l);
     }
     __syncthreads();
     for (int hi = t; hi < H * N; hi += kBlock) {
-        float* row = lg + hi * N;
+        float* row = lg + hi * ldl;
         float m = -INFINITY;
         for (int j = 0; j < N; ++j) m = fmaxf(m, row[j]);
         if (m == -INFINITY) {
@@ -166,11 +167,123 @@ __device__ void rb_attend(const float* qs, const float* ks, const float* vs, int
     __syncthreads();
     for (int e = t; e < N * D; e += kBlock) {
         const int i = e / D, c = e % D, h = c / hd;
-        const float* a = lg + (h * N + i) * N;
+        const float* a = lg + (h * N + i) * ldl;
         float s = 0.f;
 #pragma unroll 8
         for (int j = 0; j < N; ++j) s = fmaf(a[j], vs[j * ldv + c], s);
         o[e] = s;
+    }
+    __syncthreads();
+}
+
+// Steps 4-6 with register tiles, for head widths hd = D / H that are a multiple of 4: q, k [N][ld]
+// and v [N][D] with 16-byte aligned rows, logits lg [H][N][ldl] with ldl a multiple of 4 (the
+// entries past N are set to 0 here).  Each LDS read feeds several products:
+//  - logits: a lane per (head, 3 rows i, 3 rows j), nine dot products over the head's columns from
+//    16-byte reads (each q or k read serves three of them), scaled and added to the bias;
+//  - softmax: four lanes per (head, row i), each taking every fourth j; max and sum by xor shuffles
+//    within the four (a row with every pair masked becomes all zeros);
+//  - o = a v: a lane per (3 rows i, 4 columns), twelve sums over j from 16-byte reads of the
+//    probabilities and of v.
+// Rows past N in a tile read row N - 1 and are not written.
+__device__ __forceinline__ void rb_attend_tiled(const float* qs, const float* ks, const float* vs, int ld, float* lg, int ldl,
+                                int N, int D, int H, float* o) {
+    const int t = threadIdx.x, hd = D / H;
+    const float scale = 1.f / sqrtf((float)hd);
+    const int NB = (N + 2) / 3;
+    for (int e = t; e < H * NB * NB; e += kBlock) {
+        const int h = e / (NB * NB), ib = (e / NB) % NB, jb = e % NB;
+        const float *qr[3], *kr[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            qr[a] = qs + min(3 * ib + a, N - 1) * ld + h * hd;
+            kr[a] = ks + min(3 * jb + a, N - 1) * ld + h * hd;
+        }
+        float acc[3][3] = {};
+        for (int c = 0; c < hd; c += 4) {
+            float4 qv[3], kv[3];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                qv[a] = *reinterpret_cast<const float4*>(qr[a] + c);
+                kv[a] = *reinterpret_cast<const float4*>(kr[a] + c);
+            }
+#pragma unroll
+            for (int a = 0; a < 3; ++a)
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    float d = acc[a][b];
+                    d = fmaf(qv[a].x, kv[b].x, d);
+                    d = fmaf(qv[a].y, kv[b].y, d);
+                    d = fmaf(qv[a].z, kv[b].z, d);
+                    acc[a][b] = fmaf(qv[a].w, kv[b].w, d);
+                }
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = 0; b < 3; ++b) {
+                const int i = 3 * ib + a, j = 3 * jb + b;
+                if (i < N && j < N) {
+                    float* l = lg + (h * N + i) * ldl + j;
+                    const float bias = *l;
+                    *l = bias == -INFINITY ? -INFINITY : fmaf(acc[a][b], scale, bias);
+                }
+            }
+    }
+    __syncthreads();
+    for (int base = 0; base < H * N * 4; base += kBlock) {   // the same trip count in every lane
+        const int e = base + t, g = e % 4;
+        const bool act = e / 4 < H * N;
+        float* row = lg + (act ? e / 4 : 0) * ldl;
+        float m = -INFINITY;
+        if (act)
+            for (int j = g; j < N; j += 4) m = fmaxf(m, row[j]);
+        m = fmaxf(m, shfl_xor(m, 1));
+        m = fmaxf(m, shfl_xor(m, 2));
+        float z = 0.f;
+        if (act)
+            for (int j = g; j < N; j += 4) {
+                const float p = row[j] == -INFINITY ? 0.f : exp_fast(row[j] - m);
+                row[j] = p;
+                z += p;
+            }
+        z += shfl_xor(z, 1);
+        z += shfl_xor(z, 2);
+        if (act) {
+            const float rz = m == -INFINITY ? 0.f : 1.f / z;
+            for (int j = g; j < N; j += 4) row[j] *= rz;
+            if (N + g < ldl) row[N + g] = 0.f;
+        }
+    }
+    __syncthreads();
+    const int CB = D / 4;
+    for (int e = t; e < NB * CB; e += kBlock) {
+        const int ib = e / CB, c = 4 * (e % CB), h = c / hd;
+        const float* ar[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) ar[a] = lg + (h * N + min(3 * ib + a, N - 1)) * ldl;
+        float4 acc[3] = {};
+        for (int j = 0; j < N; j += 4) {
+            float4 pv[3], vv[4];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) pv[a] = *reinterpret_cast<const float4*>(ar[a] + j);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) vv[u] = *reinterpret_cast<const float4*>(vs + min(j + u, N - 1) * D + c);
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                const float pj[4] = {pv[a].x, pv[a].y, pv[a].z, pv[a].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc[a].x = fmaf(pj[u], vv[u].x, acc[a].x);
+                    acc[a].y = fmaf(pj[u], vv[u].y, acc[a].y);
+                    acc[a].z = fmaf(pj[u], vv[u].z, acc[a].z);
+                    acc[a].w = fmaf(pj[u], vv[u].w, acc[a].w);
+                }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+            if (3 * ib + a < N) *reinterpret_cast<float4*>(o + (3 * ib + a) * D + c) = acc[a];
     }
     __syncthreads();
 }
@@ -261,7 +374,7 @@ __global__ __launch_bounds__(kBlock) void relation_block_kernel(
 
     // 4-6. logits, softmax, o = a v (over xn, no longer needed)
     float* o = xn;
-    rb_attend(qs, ks, vs, ld, ld, lg, N, D, H, o);
+    rb_attend(qs, ks, vs, ld, ld, lg, N, N, D, H, o);
 
     // 7. out = x + o Wo^T  (projected into q's buffer, then the residual at the store)
     rb_project(o, N, D, wo, D, qs, ld, wbuf);
@@ -288,14 +401,16 @@ typedef float rb_f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRbFastP = 16;
 constexpr int kRbFastMaxN = 64;
 constexpr int kRbPairBatch = 8;   // pair tiles whose features a wave loads at once
+constexpr int kRbXRegs = 3;       // float4s of x a thread keeps in registers for the residual
 
 __device__ __forceinline__ rb_f32x4 rb_mfma(float a, float b, rb_f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// LDS of the matrix-core kernel (floats): three row arrays and the logits, 37 KB at the page's shape,
-// so four workgroups share a CU.  xn [N][D] holds x, then LayerNorm(x), then v; qs [N][D+1] holds q,
-// then o (row pitch D); ks [N][D+1] holds k, then o Wo^T.
+// LDS of the matrix-core kernel (floats): three row arrays and the logits, 38 KB at the page's shape,
+// so four workgroups share a CU.  xn [N][D] holds x, then LayerNorm(x), then v; qs [N][D+4] holds q,
+// then o (row pitch D); ks [N][D+4] holds k, then o Wo^T; lg [H][N][NP] the logits, rows padded to
+// NP = N rounded up to a multiple of 4 (16-byte aligned rows throughout).
 struct RbFastLayout {
     int xn, qs, ks, lg, mb, total;
 };
@@ -305,9 +420,9 @@ __host__ __device__ inline RbFastLayout rb_fast_layout(int N, int D, int H) {
     RbFastLayout L{};
     int o = 0;
     L.xn = o, o += up(N * D);
-    L.qs = o, o += up(N * (D + 1));
-    L.ks = o, o += up(N * (D + 1));
-    L.lg = o, o += up(H * N * N);
+    L.qs = o, o += N * (D + 4);
+    L.ks = o, o += N * (D + 4);
+    L.lg = o, o += H * N * up(N);
     L.mb = o, o += up(kRbFastP + H);            // b1, b2
     L.total = o;
     return L;
@@ -354,21 +469,58 @@ __device__ __forceinline__ void rb_tile_store(rb_f32x4 acc, int rt, int ct, int 
     }
 }
 
+// The w fragments of a wave's round of two tiles, t0 and t0 + 4 (those below the tile count).
+template <int KB>
+__device__ __forceinline__ void rb_wload_round(const float* __restrict__ w, int N, int D, int t0, float4 (&wv0)[KB],
+                                               float4 (&wv1)[KB]) {
+    const int CT = D / 16, T = ((N + 15) / 16) * CT, t1 = t0 + kWavesPerBlock;
+    if (t0 < T) rb_tile_wload<KB>(w, D, t0 % CT, wv0);
+    if (t1 < T) rb_tile_wload<KB>(w, D, t1 % CT, wv1);
+}
+
 // y[i, j] = sum_k a[i, k] w[j, k], i < N, j < D: a LDS [N][lda], w global [D][D] (row-major,
 // [out, in]), y LDS with row pitch ldy (y must not overlap a).  A wave takes tiles wave, wave + 4, ...
-// two at a time, with both tiles' w loads issued before the first MFMA.
+// two at a time, with both tiles' w loads issued before the first MFMA; the first round's fragments
+// come in wv0 / wv1, loaded by the caller (rb_wload_round at t0 = wave) ahead of time.
 template <int KB>
-__device__ void rb_mfma_project(const float* a, int lda, const float* __restrict__ w, int N, int D, float* y,
-                                int ldy) {
+__device__ __forceinline__ void rb_mfma_project(const float* a, int lda, const float* __restrict__ w, int N, int D,
+                                                float* y, int ldy, float4 (&wv0)[KB], float4 (&wv1)[KB]) {
     const int wave = threadIdx.x / kWave;
     const int RT = (N + 15) / 16, CT = D / 16, T = RT * CT;
     for (int t0 = wave; t0 < T; t0 += 2 * kWavesPerBlock) {
         const int t1 = t0 + kWavesPerBlock;
-        float4 wv0[KB], wv1[KB];
-        rb_tile_wload<KB>(w, D, t0 % CT, wv0);
-        if (t1 < T) rb_tile_wload<KB>(w, D, t1 % CT, wv1);
+        if (t0 != wave) rb_wload_round<KB>(w, N, D, t0, wv0, wv1);
         rb_tile_store(rb_tile_mfma<KB>(a, lda, N, D, t0 / CT, wv0), t0 / CT, t0 % CT, N, y, ldy);
         if (t1 < T) rb_tile_store(rb_tile_mfma<KB>(a, lda, N, D, t1 / CT, wv1), t1 / CT, t1 % CT, N, y, ldy);
+    }
+}
+
+template <int KB>
+__device__ __forceinline__ void rb_mfma_project(const float* a, int lda, const float* __restrict__ w, int N, int D,
+                                                float* y, int ldy) {
+    float4 wv0[KB], wv1[KB];
+    rb_wload_round<KB>(w, N, D, threadIdx.x / kWave, wv0, wv1);
+    rb_mfma_project<KB>(a, lda, w, N, D, y, ldy, wv0, wv1);
+}
+
+// LayerNorm of rows [0, N) of xn [N][D] in place (D <= 128), a wave per row, with the lane's
+// scale and shift (columns lane and lane + 64) already in registers.
+__device__ __forceinline__ void rb_layernorm_regs(float* xn, int N, int D, const float (&g)[2], const float (&be)[2], float eps) {
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    for (int i = w; i < N; i += kWavesPerBlock) {
+        float* r = xn + i * D;
+        const float v0 = lane < D ? r[lane] : 0.f, v1 = lane + kWave < D ? r[lane + kWave] : 0.f;
+        float s = lane < D ? v0 + v1 : 0.f;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) s += shfl_xor(s, o);
+        const float mean = s / D;
+        const float c0 = lane < D ? v0 - mean : 0.f, c1 = lane + kWave < D ? v1 - mean : 0.f;
+        float v2 = fmaf(c1, c1, c0 * c0);
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) v2 += shfl_xor(v2, o);
+        const float rstd = 1.f / sqrtf(v2 / D + eps);
+        if (lane < D) r[lane] = c0 * rstd * g[0] + be[0];
+        if (lane + kWave < D) r[lane + kWave] = c1 * rstd * g[1] + be[1];
     }
 }
 
@@ -412,30 +564,65 @@ __global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
     const int b = blockIdx.x;
     const int t = threadIdx.x, lane = lane_id(), wave = t / kWave;
     const int li = lane % 16, lk = 4 * (lane / 16);
-    const int ND = N * D, NN = N * N, ld = D + 1;
+    const int ND = N * D, NN = N * N, ld = D + 4, NP = (N + 3) & ~3;
     const RbFastLayout L = rb_fast_layout(N, D, H);
     float* xn = lds + L.xn;          // [N][D]: x, LayerNorm(x), then v
     float* qs = lds + L.qs;          // [N][ld]: q, then o (pitch D)
     float* ks = lds + L.ks;          // [N][ld]: k, then o Wo^T
-    float* lg = lds + L.lg;          // [H][N][N]
+    float* lg = lds + L.lg;          // [H][N][NP]
     float* mb = lds + L.mb;          // b1 [16], b2 [H]
     const float* x = nodes + (int64_t)b * ND;
 
-    // 0. x and the MLP biases into LDS
-    for (int e = t; e < ND / 4; e += kBlock)
-        reinterpret_cast<float4*>(xn)[e] = reinterpret_cast<const float4*>(x)[e];
+    // 0. Every load that does not depend on another goes out first, so their latencies overlap: x
+    // (the thread's first kRbXRegs float4s stay in registers for the residual), the MLP weights, the
+    // first batch of pair features and mask entries (step 1), the lane's LayerNorm scale and shift.
+    // Then x and the MLP biases into LDS.
+    // (at 128 columns the registers go to the projections: x is read again for the residual)
+    constexpr int XR = KB <= 6 ? kRbXRegs : 0;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    float4 xr[XR > 0 ? XR : 1];
+#pragma unroll
+    for (int u = 0; u < XR; ++u)
+        if (t + u * kBlock < ND / 4) xr[u] = x4[t + u * kBlock];
+    const float4 w1f = *reinterpret_cast<const float4*>(w1 + li * kRbFastP + lk);
+    const float4 w2f = li < H ? *reinterpret_cast<const float4*>(w2 + li * kRbFastP + lk)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* fp = pair + (int64_t)b * NN * kRbFastP;
+    const float* mg = mask + (int64_t)b * NN;
+    const int PT = (NN + 15) / 16;
+    float4 fb[kRbPairBatch];
+    float kb[kRbPairBatch];
+    // pair tiles pt0 + 4u of this wave: the features of pair pt * 16 + li (k = lk .. lk + 3) and its mask
+    auto load_batch = [&](int pt0) {
+#pragma unroll
+        for (int u = 0; u < kRbPairBatch; ++u) {
+            const int p = (pt0 + u * kWavesPerBlock) * 16 + li;
+            fb[u] = p < NN ? *reinterpret_cast<const float4*>(fp + (int64_t)p * kRbFastP + lk)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            kb[u] = p < NN ? mg[p] : 0.f;
+        }
+    };
+    load_batch(wave);
+    float gr[2], br[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int d = lane + u * kWave;
+        gr[u] = d < D ? gamma[d] : 0.f;
+        br[u] = d < D ? beta[d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < XR; ++u)
+        if (t + u * kBlock < ND / 4) reinterpret_cast<float4*>(xn)[t + u * kBlock] = xr[u];
+    for (int e = t + XR * kBlock; e < ND / 4; e += kBlock) reinterpret_cast<float4*>(xn)[e] = x4[e];
     if (t < kRbFastP) mb[t] = b1[t];
     if (t < H) mb[kRbFastP + t] = b2[t];
     __syncthreads();
 
     // 1. pair bias into the logit buffer (-inf where masked), 16 pairs per wave step
     {
-        const float4 w1f = *reinterpret_cast<const float4*>(w1 + li * kRbFastP + lk);
-        const float4 w2f = li < H ? *reinterpret_cast<const float4*>(w2 + li * kRbFastP + lk)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float* fp = pair + (int64_t)b * NN * kRbFastP;
-        const float* mg = mask + (int64_t)b * NN;
-        const int PT = (NN + 15) / 16;
+        // pair p = i N + j: i = floor((p + 0.5) / N) in float is exact for p < 2^12 (the error,
+        // below 1e-5, is far from the 0.5 / N gap to an integer)
+        const float inv_n = 1.f / (float)N;
         // pairs pt*16 .. +15 with the features f of pair pt*16 + li (k = lk .. lk + 3) and its mask
         auto tile = [&](int pt, const float4& f, float keepv) {
             const int p = pt * 16 + li;
@@ -448,7 +635,7 @@ __global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float hs = h[r] + mb[lk + r];
-                sl[r] = hs / (1.f + exp_fast(-hs));
+                sl[r] = hs * __builtin_amdgcn_rcpf(1.f + exp_fast(-hs));   // SiLU; rcp within 1 ulp
             }
             rb_f32x4 c = {0.f, 0.f, 0.f, 0.f};
             c = rb_mfma(w2f.x, sl[0], c);
@@ -457,49 +644,61 @@ __global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
             c = rb_mfma(w2f.w, sl[3], c);
             if (p < NN) {
                 const bool keep = keepv >= 0.5f;
+                const int i = (int)(((float)p + 0.5f) * inv_n);
+                float* lp = lg + i * NP + (p - i * N);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int h2 = lk + r;
-                    if (h2 < H) lg[h2 * NN + p] = keep ? c[r] + mb[kRbFastP + h2] : -INFINITY;
+                    if (h2 < H) lp[h2 * N * NP] = keep ? c[r] + mb[kRbFastP + h2] : -INFINITY;
                 }
             }
         };
         // the features and mask entries of kRbPairBatch tiles are loaded together, then consumed: one
-        // memory latency per batch instead of one per tile
+        // memory latency per batch instead of one per tile (the first batch went out in step 0)
         for (int pt0 = wave; pt0 < PT; pt0 += kRbPairBatch * kWavesPerBlock) {
-            float4 fb[kRbPairBatch];
-            float kb[kRbPairBatch];
-#pragma unroll
-            for (int u = 0; u < kRbPairBatch; ++u) {
-                const int p = (pt0 + u * kWavesPerBlock) * 16 + li;
-                fb[u] = p < NN ? *reinterpret_cast<const float4*>(fp + (int64_t)p * kRbFastP + lk)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-                kb[u] = p < NN ? mg[p] : 0.f;
-            }
+            if (pt0 != wave) load_batch(pt0);
 #pragma unroll
             for (int u = 0; u < kRbPairBatch; ++u)
                 if (pt0 + u * kWavesPerBlock < PT) tile(pt0 + u * kWavesPerBlock, fb[u], kb[u]);
         }
     }
 
+    // the first round of q's weight fragments, in flight during the LayerNorm (up to 96 columns: at
+    // 128 the 64 registers they take would spill)
+    float4 wa[KB], wb[KB];
+    if constexpr (KB <= 6) rb_wload_round<KB>(wq, N, D, wave, wa, wb);
+
     // 2. LayerNorm in place
-    rb_layernorm(xn, N, D, gamma, beta, eps);
+    rb_layernorm_regs(xn, N, D, gr, br, eps);
     __syncthreads();
+    if constexpr (KB > 6) rb_wload_round<KB>(wq, N, D, wave, wa, wb);
 
     // 3. q, k into their buffers, then v over LayerNorm(x) (all reads of xn before the writes)
-    rb_mfma_project<KB>(xn, D, wq, N, D, qs, ld);
+    rb_mfma_project<KB>(xn, D, wq, N, D, qs, ld, wa, wb);
     rb_mfma_project<KB>(xn, D, wk, N, D, ks, ld);
     rb_mfma_project_in_place<KB>(xn, D, wv, N, D);
     __syncthreads();
 
     // 4-6. logits, softmax, o = a v into q's buffer (q is no longer read once the logits exist)
-    rb_attend(qs, ks, xn, ld, D, lg, N, D, H, qs);
+    if ((D / H) % 4 == 0)
+        rb_attend_tiled(qs, ks, xn, ld, lg, NP, N, D, H, qs);
+    else
+        rb_attend(qs, ks, xn, ld, D, lg, NP, N, D, H, qs);
 
     // 7. out = x + o Wo^T (projected into k's buffer, then the residual at the store)
     rb_mfma_project<KB>(qs, D, wo, N, D, ks, ld);
     __syncthreads();
-    float* ob = out + (int64_t)b * ND;
-    for (int e = t; e < ND; e += kBlock) ob[e] = x[e] + ks[(e / D) * ld + e % D];
+    float4* ob4 = reinterpret_cast<float4*>(out + (int64_t)b * ND);
+    const int D4 = D / 4;
+    auto residual = [&](int e, const float4& xv) {
+        const int i = e / D4, c = 4 * (e - i * D4);
+        const float4 y = *reinterpret_cast<const float4*>(ks + i * ld + c);
+        ob4[e] = make_float4(xv.x + y.x, xv.y + y.y, xv.z + y.z, xv.w + y.w);
+    };
+#pragma unroll
+    for (int u = 0; u < XR; ++u)
+        if (t + u * kBlock < ND / 4) residual(t + u * kBlock, xr[u]);
+    for (int e = t + XR * kBlock; e < ND / 4; e += kBlock) residual(e, x4[e]);
 }
 
 }  // namespace
