@@ -238,8 +238,8 @@ __device__ __forceinline__ void rb_attend_tiled(const float* qs, const float* ks
         float m = -INFINITY;
         if (act)
             for (int j = g; j < N; j += 4) m = fmaxf(m, row[j]);
-        m = fmaxf(m, shfl_xor(m, 1));
-        m = fmaxf(m, shfl_xor(m, 2));
+        m = fmaxf(m, dpp<0xB1>(m));   // quad_perm [1,0,3,2]: the four lanes of a row are a quad
+        m = fmaxf(m, dpp<0x4E>(m));   // quad_perm [2,3,0,1]
         float z = 0.f;
         if (act)
             for (int j = g; j < N; j += 4) {
@@ -247,8 +247,7 @@ __device__ __forceinline__ void rb_attend_tiled(const float* qs, const float* ks
                 row[j] = p;
                 z += p;
             }
-        z += shfl_xor(z, 1);
-        z += shfl_xor(z, 2);
+        z = group_sum<4>(z);
         if (act) {
             const float rz = m == -INFINITY ? 0.f : 1.f / z;
             for (int j = g; j < N; j += 4) row[j] *= rz;
@@ -432,26 +431,28 @@ __host__ __device__ inline RbFastLayout rb_fast_layout(int N, int D, int H) {
 // One 16x16 tile of y = a w^T over KB blocks of 16 k: a [N][lda] in LDS, w [D][D] in global memory;
 // k past D and rows past N read 0.  The w fragments of a tile are loaded first (one L2 round trip),
 // the a fragments from LDS as each block is reached.
-template <int KB>
+template <int KB, bool EX>
 __device__ __forceinline__ void rb_tile_wload(const float* __restrict__ w, int D, int ct, float4 (&wv)[KB]) {
     const int lane = lane_id(), li = lane % 16, lk = 4 * (lane / 16);
     const float* wr = w + (int64_t)(ct * 16 + li) * D + lk;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-        wv[kb] = 16 * kb + lk < D ? *reinterpret_cast<const float4*>(wr + 16 * kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+        wv[kb] = EX || 16 * kb + lk < D ? *reinterpret_cast<const float4*>(wr + 16 * kb)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <int KB>
+template <int KB, bool EX>
 __device__ __forceinline__ rb_f32x4 rb_tile_mfma(const float* a, int lda, int N, int D, int rt,
                                                  const float4 (&wv)[KB]) {
     const int lane = lane_id(), li = lane % 16, lk = 4 * (lane / 16);
-    const int row = rt * 16 + li;
-    const float* ar = a + row * lda + lk;
+    // rows past N repeat row N - 1: a row of the product depends on its own row of a only, and
+    // those rows are never stored
+    const float* ar = a + min(rt * 16 + li, N - 1) * lda + lk;
     rb_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-        const float4 av = row < N && 16 * kb + lk < D ? *reinterpret_cast<const float4*>(ar + 16 * kb)
-                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 av = EX || 16 * kb + lk < D ? *reinterpret_cast<const float4*>(ar + 16 * kb)
+                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
         acc = rb_mfma(av.x, wv[kb].x, acc);
         acc = rb_mfma(av.y, wv[kb].y, acc);
         acc = rb_mfma(av.z, wv[kb].z, acc);
@@ -470,55 +471,85 @@ __device__ __forceinline__ void rb_tile_store(rb_f32x4 acc, int rt, int ct, int 
 }
 
 // The w fragments of a wave's round of two tiles, t0 and t0 + 4 (those below the tile count).
-template <int KB>
+template <int KB, bool EX>
 __device__ __forceinline__ void rb_wload_round(const float* __restrict__ w, int N, int D, int t0, float4 (&wv0)[KB],
                                                float4 (&wv1)[KB]) {
-    const int CT = D / 16, T = ((N + 15) / 16) * CT, t1 = t0 + kWavesPerBlock;
-    if (t0 < T) rb_tile_wload<KB>(w, D, t0 % CT, wv0);
-    if (t1 < T) rb_tile_wload<KB>(w, D, t1 % CT, wv1);
+    const int CT = EX ? KB : D / 16, T = ((N + 15) / 16) * CT, t1 = t0 + kWavesPerBlock;
+    if (t0 < T) rb_tile_wload<KB, EX>(w, D, t0 % CT, wv0);
+    if (t1 < T) rb_tile_wload<KB, EX>(w, D, t1 % CT, wv1);
 }
 
 // y[i, j] = sum_k a[i, k] w[j, k], i < N, j < D: a LDS [N][lda], w global [D][D] (row-major,
 // [out, in]), y LDS with row pitch ldy (y must not overlap a).  A wave takes tiles wave, wave + 4, ...
 // two at a time, with both tiles' w loads issued before the first MFMA; the first round's fragments
 // come in wv0 / wv1, loaded by the caller (rb_wload_round at t0 = wave) ahead of time.
-template <int KB>
+template <int KB, bool EX>
 __device__ __forceinline__ void rb_mfma_project(const float* a, int lda, const float* __restrict__ w, int N, int D,
                                                 float* y, int ldy, float4 (&wv0)[KB], float4 (&wv1)[KB]) {
     const int wave = threadIdx.x / kWave;
-    const int RT = (N + 15) / 16, CT = D / 16, T = RT * CT;
+    const int RT = (N + 15) / 16, CT = EX ? KB : D / 16, T = RT * CT;
     for (int t0 = wave; t0 < T; t0 += 2 * kWavesPerBlock) {
         const int t1 = t0 + kWavesPerBlock;
-        if (t0 != wave) rb_wload_round<KB>(w, N, D, t0, wv0, wv1);
-        rb_tile_store(rb_tile_mfma<KB>(a, lda, N, D, t0 / CT, wv0), t0 / CT, t0 % CT, N, y, ldy);
-        if (t1 < T) rb_tile_store(rb_tile_mfma<KB>(a, lda, N, D, t1 / CT, wv1), t1 / CT, t1 % CT, N, y, ldy);
+        if (t0 != wave) rb_wload_round<KB, EX>(w, N, D, t0, wv0, wv1);
+        rb_tile_store(rb_tile_mfma<KB, EX>(a, lda, N, D, t0 / CT, wv0), t0 / CT, t0 % CT, N, y, ldy);
+        if (t1 < T) rb_tile_store(rb_tile_mfma<KB, EX>(a, lda, N, D, t1 / CT, wv1), t1 / CT, t1 % CT, N, y, ldy);
     }
 }
 
-template <int KB>
+template <int KB, bool EX>
 __device__ __forceinline__ void rb_mfma_project(const float* a, int lda, const float* __restrict__ w, int N, int D,
                                                 float* y, int ldy) {
     float4 wv0[KB], wv1[KB];
-    rb_wload_round<KB>(w, N, D, threadIdx.x / kWave, wv0, wv1);
-    rb_mfma_project<KB>(a, lda, w, N, D, y, ldy, wv0, wv1);
+    rb_wload_round<KB, EX>(w, N, D, threadIdx.x / kWave, wv0, wv1);
+    rb_mfma_project<KB, EX>(a, lda, w, N, D, y, ldy, wv0, wv1);
+}
+
+// Projections as a stream of tiles, software-pipelined one tile ahead: a wave's tiles u = wave,
+// wave + 4, ... run in order, and tile m + 1's w fragments load while tile m's MFMAs run, in two
+// register sets used alternately (wa holds the first tile's, loaded ahead of time by the caller
+// with rb_stream_first), so a wave waits for L2 once per stream rather than once per round.
+//
+// Up to two products over the same a: tiles [0, T) are y0 = a w0^T, tiles [T, 2T) y1 = a w1^T
+// (w1 == nullptr: one product); T = row tiles x column tiles.
+template <int KB, bool EX>
+__device__ __forceinline__ void rb_stream_first(const float* __restrict__ w0, int N, int D, float4 (&wa)[KB]) {
+    const int wave = threadIdx.x / kWave, CT = EX ? KB : D / 16, T = ((N + 15) / 16) * CT;
+    if (wave < T) rb_tile_wload<KB, EX>(w0, D, wave % CT, wa);
+}
+
+template <int KB, bool EX>
+__device__ __forceinline__ void rb_mfma_stream(const float* a, int lda, const float* __restrict__ w0, float* y0,
+                                               const float* __restrict__ w1, float* y1, int N, int D, int ldy,
+                                               float4 (&wa)[KB], float4 (&wb)[KB]) {
+    const int wave = threadIdx.x / kWave;
+    const int CT = EX ? KB : D / 16, T = ((N + 15) / 16) * CT, U = (w1 ? 2 : 1) * T;
+    auto load = [&](int u, float4 (&wv)[KB]) { rb_tile_wload<KB, EX>(u < T ? w0 : w1, D, (u % T) % CT, wv); };
+    auto run = [&](int u, const float4 (&wv)[KB]) {
+        const int l = u % T;
+        rb_tile_store(rb_tile_mfma<KB, EX>(a, lda, N, D, l / CT, wv), l / CT, l % CT, N, u < T ? y0 : y1, ldy);
+    };
+    for (int u = wave; u < U; u += 2 * kWavesPerBlock) {
+        const int u1 = u + kWavesPerBlock, u2 = u1 + kWavesPerBlock;
+        if (u1 < U) load(u1, wb);
+        run(u, wa);
+        if (u1 >= U) break;
+        if (u2 < U) load(u2, wa);
+        run(u1, wb);
+    }
 }
 
 // LayerNorm of rows [0, N) of xn [N][D] in place (D <= 128), a wave per row, with the lane's
 // scale and shift (columns lane and lane + 64) already in registers.
 __device__ __forceinline__ void rb_layernorm_regs(float* xn, int N, int D, const float (&g)[2], const float (&be)[2], float eps) {
     const int lane = lane_id(), w = threadIdx.x / kWave;
+    const float inv_d = 1.f / (float)D;
     for (int i = w; i < N; i += kWavesPerBlock) {
         float* r = xn + i * D;
         const float v0 = lane < D ? r[lane] : 0.f, v1 = lane + kWave < D ? r[lane + kWave] : 0.f;
-        float s = lane < D ? v0 + v1 : 0.f;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) s += shfl_xor(s, o);
-        const float mean = s / D;
+        const float mean = group_sum<kWave>(v0 + v1) * inv_d;
         const float c0 = lane < D ? v0 - mean : 0.f, c1 = lane + kWave < D ? v1 - mean : 0.f;
-        float v2 = fmaf(c1, c1, c0 * c0);
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) v2 += shfl_xor(v2, o);
-        const float rstd = 1.f / sqrtf(v2 / D + eps);
+        const float var = group_sum<kWave>(fmaf(c1, c1, c0 * c0)) * inv_d;
+        const float rstd = __builtin_amdgcn_rsqf(var + eps);   // within 1 ulp
         if (lane < D) r[lane] = c0 * rstd * g[0] + be[0];
         if (lane + kWave < D) r[lane + kWave] = c1 * rstd * g[1] + be[1];
     }
@@ -527,22 +558,22 @@ __device__ __forceinline__ void rb_layernorm_regs(float* xn, int N, int D, const
 // The same product written over a itself (y = a, row pitch lda): every tile is computed into
 // registers first, then after a workgroup barrier -- every wave's reads of a done -- written.  All
 // threads must call it.
-template <int KB>
+template <int KB, bool EX>
 __device__ void rb_mfma_project_in_place(float* a, int lda, const float* __restrict__ w, int N, int D) {
     // at most (kRbFastMaxN / 16) row tiles x KB column tiles over the four waves
     constexpr int kRbMaxTilesPerWave = (kRbFastMaxN / 16) * KB / kWavesPerBlock;
     const int wave = threadIdx.x / kWave;
-    const int RT = (N + 15) / 16, CT = D / 16, T = RT * CT;
+    const int RT = (N + 15) / 16, CT = EX ? KB : D / 16, T = RT * CT;
     rb_f32x4 acc[kRbMaxTilesPerWave];
 #pragma unroll
     for (int u = 0; u < kRbMaxTilesPerWave; u += 2) {
         const int t0 = wave + u * kWavesPerBlock, t1 = t0 + kWavesPerBlock;
         if (t0 >= T) break;
         float4 wv0[KB], wv1[KB];
-        rb_tile_wload<KB>(w, D, t0 % CT, wv0);
-        if (t1 < T) rb_tile_wload<KB>(w, D, t1 % CT, wv1);
-        acc[u] = rb_tile_mfma<KB>(a, lda, N, D, t0 / CT, wv0);
-        if (t1 < T) acc[u + 1] = rb_tile_mfma<KB>(a, lda, N, D, t1 / CT, wv1);
+        rb_tile_wload<KB, EX>(w, D, t0 % CT, wv0);
+        if (t1 < T) rb_tile_wload<KB, EX>(w, D, t1 % CT, wv1);
+        acc[u] = rb_tile_mfma<KB, EX>(a, lda, N, D, t0 / CT, wv0);
+        if (t1 < T) acc[u + 1] = rb_tile_mfma<KB, EX>(a, lda, N, D, t1 / CT, wv1);
     }
     __syncthreads();
 #pragma unroll
@@ -553,7 +584,7 @@ __device__ void rb_mfma_project_in_place(float* a, int lda, const float* __restr
     }
 }
 
-template <int KB>
+template <int KB, bool EX>
 __global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
     const float* nodes, const float* __restrict__ pair, const float* __restrict__ mask,
     const float* __restrict__ gamma, const float* __restrict__ beta, float eps, const float* __restrict__ wq,
@@ -663,21 +694,19 @@ __global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
         }
     }
 
-    // the first round of q's weight fragments, in flight during the LayerNorm (up to 96 columns: at
-    // 128 the 64 registers they take would spill)
+    // q's first weight tile, in flight during the LayerNorm
     float4 wa[KB], wb[KB];
-    if constexpr (KB <= 6) rb_wload_round<KB>(wq, N, D, wave, wa, wb);
+    rb_stream_first<KB, EX>(wq, N, D, wa);
 
     // 2. LayerNorm in place
     rb_layernorm_regs(xn, N, D, gr, br, eps);
     __syncthreads();
-    if constexpr (KB > 6) rb_wload_round<KB>(wq, N, D, wave, wa, wb);
 
     // 3. q, k into their buffers, then v over LayerNorm(x) (all reads of xn before the writes)
-    rb_mfma_project<KB>(xn, D, wq, N, D, qs, ld, wa, wb);
-    rb_mfma_project<KB>(xn, D, wk, N, D, ks, ld);
-    rb_mfma_project_in_place<KB>(xn, D, wv, N, D);
+    rb_mfma_stream<KB, EX>(xn, D, wq, qs, wk, ks, N, D, ld, wa, wb);
+    rb_mfma_project_in_place<KB, EX>(xn, D, wv, N, D);
     __syncthreads();
+
 
     // 4-6. logits, softmax, o = a v into q's buffer (q is no longer read once the logits exist)
     if ((D / H) % 4 == 0)
@@ -686,7 +715,7 @@ __global__ __launch_bounds__(kBlock, 4) void relation_block_mfma_kernel(
         rb_attend(qs, ks, xn, ld, D, lg, NP, N, D, H, qs);
 
     // 7. out = x + o Wo^T (projected into k's buffer, then the residual at the store)
-    rb_mfma_project<KB>(qs, D, wo, N, D, ks, ld);
+    rb_mfma_project<KB, EX>(qs, D, wo, N, D, ks, ld);
     __syncthreads();
     float4* ob4 = reinterpret_cast<float4*>(out + (int64_t)b * ND);
     const int D4 = D / 4;
@@ -707,20 +736,20 @@ size_t relation_block_lds_bytes(int N, int D, int H, int P) { return (size_t)rb_
 
 namespace {
 
-template <int KB>
+template <int KB, bool EX>
 hipError_t launch_rb_fast(const float* nodes, const float* pair, const float* mask, const float* gamma,
                           const float* beta, float eps, const float* wq, const float* wk, const float* wv,
                           const float* wo, const float* w1, const float* b1, const float* w2, const float* b2,
                           int64_t B, int N, int D, int H, float* out, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(relation_block_mfma_kernel<KB>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(relation_block_mfma_kernel<KB, EX>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kRbMaxLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const size_t lds = (size_t)rb_fast_layout(N, D, H).total * 4;
-    hipLaunchKernelGGL(relation_block_mfma_kernel<KB>, dim3((unsigned)B), dim3(kBlock), lds, stream, nodes, pair,
+    hipLaunchKernelGGL((relation_block_mfma_kernel<KB, EX>), dim3((unsigned)B), dim3(kBlock), lds, stream, nodes, pair,
                        mask, gamma, beta, eps, wq, wk, wv, wo, w1, b1, w2, b2, N, D, H, out);
     return hipGetLastError();
 }
@@ -737,9 +766,14 @@ hipError_t launch_relation_block(const float* nodes, const float* pair, const fl
     // the matrix-core kernel where its shape conditions hold (16-byte operand loads included)
     if (P == kRbFastP && D % 16 == 0 && D <= 128 && N <= kRbFastMaxN && aligned16(pair) && aligned16(w1) &&
         aligned16(w2) && (size_t)rb_fast_layout(N, D, H).total * 4 <= kRbMaxLds) {
+        // KB blocks of 16 columns; EX: D = 16 KB exactly (no column bounds to test)
         auto go = [&](auto kb) {
-            return launch_rb_fast<decltype(kb)::value>(nodes, pair, mask, gamma, beta, eps, wq, wk, wv, wo, w1, b1,
-                                                       w2, b2, B, N, D, H, out, stream);
+            constexpr int KB = decltype(kb)::value;
+            if (D == 16 * KB)
+                return launch_rb_fast<KB, true>(nodes, pair, mask, gamma, beta, eps, wq, wk, wv, wo, w1, b1, w2, b2,
+                                                B, N, D, H, out, stream);
+            return launch_rb_fast<KB, false>(nodes, pair, mask, gamma, beta, eps, wq, wk, wv, wo, w1, b1, w2, b2, B,
+                                             N, D, H, out, stream);
         };
         if (D <= 32) return go(std::integral_constant<int, 2>{});
         if (D <= 64) return go(std::integral_constant<int, 4>{});
