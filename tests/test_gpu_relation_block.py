@@ -1,6 +1,8 @@
 """The dense relation-biased attention block (the l2_p4 page) on the GPU against the oracle: the
 page's shapes with every pair attending, random masks, rows with no pair kept (which return the
-node row), other shapes up to the LDS limit, a large batch, and in place."""
+node row), other shapes up to the LDS limit (widths that are and are not whole 16-column blocks,
+head widths that are and are not multiples of 4, node counts that are not), the 4096-element
+batch the benchmark times, and in place."""
 import numpy as np
 import pytest
 import torch
@@ -37,10 +39,18 @@ def test_page_shapes(mask):
 @pytest.mark.parametrize("shape", [(2, 7, 32, 2, 8), (1, 1, 16, 1, 4), (3, 33, 64, 8, 5), (2, 40, 128, 8, 16),
                                    (1, 17, 48, 16, 3), (256, 24, 96, 4, 16), (3, 64, 64, 2, 16),
                                    (5, 1, 32, 1, 16), (2, 17, 48, 3, 16), (7, 33, 64, 8, 16), (2, 65, 64, 4, 16),
-                                   (2, 20, 160, 4, 16)], ids=str)
+                                   (2, 20, 160, 4, 16), (3, 48, 80, 4, 16), (2, 30, 112, 8, 16),
+                                   (4, 26, 128, 4, 16)], ids=str)
 def test_other_shapes(shape):
     got, want, _, _ = _run(*shape, 52, "random")
     assert_close(got, want, "f32", f"relation block {shape}")
+
+
+def test_benchmark_batch_every_element():
+    """The 4096-element batch the benchmark times (the page's shape, every pair attending), every
+    element against the oracle."""
+    got, want, _, _ = _run(4096, PAGE["N"], PAGE["D"], PAGE["H"], PAGE["P"], 0, "ones")
+    assert_close(got, want, "f32", "relation block, 4096 elements")
 
 
 @pytest.mark.parametrize("mask", ["ones", "random_empty"])
