@@ -291,6 +291,13 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
     }
 }
 
+// Grid cap of the segment kernel (a wave per segment, striding past 2^16 waves).  The table's
+// capacity counts every row that could be long (E / (short_max + 1) of them), several times the
+// segments a power-law graph has, and the workgroups past the real count still cost dispatch time:
+// at c4 (2^24 edges) 16384 workgroups took the kernel from 72 to 62 us; at c5 (2^26 edges, 74k
+// segments) it made no difference, and smaller caps lost there (4096: +60 us).
+constexpr int64_t kSoftmaxSegmentGrid = 16384;
+
 constexpr int kSegRegs = 16;                      // floats each lane holds of a segment chunk
 constexpr int kWaveChunk = kSegRegs * kWave;       // 1024 floats per chunk
 
@@ -504,7 +511,7 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         }
         if (plan)
             hipLaunchKernelGGL(softmax_segment_kernel<HH>,
-                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kSegmentGrid)),
+                               dim3(grid_for(plan->seg_capacity, kWavesPerBlock, kSoftmaxSegmentGrid)),
                                dim3(kBlock), 0, stream, scores, out, *plan);
         if (plan)
             hipLaunchKernelGGL(softmax_hub_write_kernel<HH>,
