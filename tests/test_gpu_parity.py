@@ -411,14 +411,17 @@ def test_tables_above_4gib_use_64bit_offsets(orc):
 
 @pytest.mark.timeout(400)
 def test_c5_edge_softmax_full_size(orc):
-    """Edge softmax on the skew-stress graph (200k-edge hubs split into merged segments)."""
+    """Edge softmax on the skew-stress graph (200k-edge hubs split into merged segments): sampled
+    rows plus every hub row (84 % of the edges; the segment walk takes more than one grid stride
+    here, and its later strides are hub segments)."""
     w = G.WORKLOADS["c5"]
     g = G.make_graph(w, 0)
     s = G.make_scores(w, g.n_edges, 0)
     rp = to_dev(g.row_ptr)
     plan = gat.gat_plan_build(rp, g.n_edges, w.heads, w.head_dim)
     alpha = to_np(gat.gat_edge_softmax(rp, to_dev(s), plan=plan))
-    rows = G.sample_rows(g, 256, 3)
+    seg_len = plan.struct.seg_len
+    rows = np.unique(np.concatenate([G.sample_rows(g, 256, 3), np.flatnonzero(g.degrees() > seg_len)]))
     sub_rp, _, eids = G.take_rows(g, rows)
     assert_close(alpha[eids], orc.edge_softmax(sub_rp, s[eids]), "f32", "c5 softmax")
 
