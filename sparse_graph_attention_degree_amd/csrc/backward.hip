@@ -440,12 +440,14 @@ __device__ __forceinline__ float block_head_sum(float s, float (*ls)[H]) {
 // alpha and grad (lane l holds elements l, l+64, ..., all of head l % H), the per-head dot is a
 // per-lane sum and an xor-shuffle tree over the head's lanes; a one-chunk long row is written from
 // registers, a longer one is read again; a hub segment leaves its per-head dot in the partial
-// buffer.
+// buffer.  One register set per lane holds alpha and grad of one chunk.  Left to itself the
+// compiler keeps the first pass's registers apart from the write pass's and takes about 108
+// VGPRs (4 waves per SIMD); asking for 6 waves per SIMD packs it into 80 without spilling.
 constexpr int kSbSegRegs = 16;
 constexpr int kSbChunk = kSbSegRegs * kWave;
 
 template <int H>
-__global__ __launch_bounds__(kBlock) void softmax_bwd_segment_kernel(const float* alpha, const float* grad,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void softmax_bwd_segment_kernel(const float* alpha, const float* grad,
                                                                      float* out, PlanView plan, float scale) {
     const int lane = lane_id();
     const int64_t n_segs = plan.counts[kNSegs];
@@ -456,15 +458,40 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_segment_kernel(const float
         const int4 sg = plan.segs[s];
         const int64_t n = (int64_t)(sg.z - sg.y) * H;
         const int64_t off = (int64_t)sg.y * H;
+        // floats of the chunk at c0, 0 past the end (its loads then read 0 and move no data)
+        auto chunk_len = [&](int64_t c0) {
+            return opaque_uniform((int)(n - c0 <= 0 ? 0 : (n - c0 < kSbChunk ? n - c0 : kSbChunk)));
+        };
+        // a chunk of alpha and grad, every load issued (past the end: 0), so the compiler counts
+        // them exactly and a wait for one chunk never covers the next one's loads
+        auto load_chunk = [&](float(&x)[kSbSegRegs], float(&y)[kSbSegRegs], int64_t c0, int cn) {
+            const __amdgpu_buffer_rsrc_t ra = span(alpha + off + c0, (int64_t)cn * 4);
+            const __amdgpu_buffer_rsrc_t rg = span(grad + off + c0, (int64_t)cn * 4);
+            const int b = opaque(lane * 4);
+#pragma unroll
+            for (int k = 0; k < kSbSegRegs; ++k) x[k] = bload(ra, b + k * kWave * 4);
+#pragma unroll
+            for (int k = 0; k < kSbSegRegs; ++k) y[k] = bload(rg, b + k * kWave * 4);
+        };
+        auto dot_chunk = [&](const float(&x)[kSbSegRegs], const float(&y)[kSbSegRegs], float& d) {
+#pragma unroll
+            for (int k = 0; k < kSbSegRegs; ++k) d = fmaf(x[k], y[k], d);   // 0 past the end
+        };
+        auto store_chunk = [&](const float(&x)[kSbSegRegs], const float(&y)[kSbSegRegs], int64_t c0, int cn,
+                               float d) {
+            const __amdgpu_buffer_rsrc_t dst = span(out + off + c0, (int64_t)cn * 4);
+            const int b = opaque(lane * 4);
+#pragma unroll
+            for (int k = 0; k < kSbSegRegs; ++k) bstore(dst, scale * x[k] * (y[k] - d), b + k * kWave * 4);
+        };
         float a[kSbSegRegs], g[kSbSegRegs];
         float dot = 0.f;
+        int cv = 0;
 #pragma unroll 1
         for (int64_t c0 = 0; c0 < n; c0 += kSbChunk) {
-            const int cn = (int)(n - c0 < kSbChunk ? n - c0 : kSbChunk);
-            load_run(span(alpha + off + c0, (int64_t)cn * 4), cn, lane, a);
-            load_run(span(grad + off + c0, (int64_t)cn * 4), cn, lane, g);
-#pragma unroll
-            for (int k = 0; k < kSbSegRegs; ++k) dot = fmaf(a[k], g[k], dot);   // 0 past the end
+            cv = chunk_len(c0);
+            load_chunk(a, g, c0, cv);
+            dot_chunk(a, g, dot);
         }
 #pragma unroll
         for (int o = H; o < kWave; o <<= 1) dot += shfl_xor(dot, o);
@@ -472,17 +499,20 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_segment_kernel(const float
             if (lane < H) plan.partials[(int64_t)sg.w * plan.state_floats + lane] = dot;
             continue;
         }
-#pragma unroll 1
-        for (int64_t c0 = 0; c0 < n; c0 += kSbChunk) {
-            const int cn = (int)(n - c0 < kSbChunk ? n - c0 : kSbChunk);
-            if (n > kSbChunk) {
-                load_run(span(alpha + off + c0, (int64_t)cn * 4), cn, lane, a);
-                load_run(span(grad + off + c0, (int64_t)cn * 4), cn, lane, g);
-            }
-            const __amdgpu_buffer_rsrc_t dst = span(out + off + c0, (int64_t)cn * 4);
+        if (n <= kSbChunk) {
+            // still in registers; only the stores that hold data are issued
+            const __amdgpu_buffer_rsrc_t dst = span(out + off, (int64_t)cv * 4);
+            const int b = opaque(lane * 4);
 #pragma unroll
             for (int k = 0; k < kSbSegRegs; ++k)
-                if (k * kWave < cn) bstore(dst, scale * a[k] * (g[k] - dot), (lane + k * kWave) * 4);
+                if (k * kWave < cv) bstore(dst, scale * a[k] * (g[k] - dot), b + k * kWave * 4);
+            continue;
+        }
+#pragma unroll 1
+        for (int64_t c0 = 0; c0 < n; c0 += kSbChunk) {
+            cv = chunk_len(c0);
+            load_chunk(a, g, c0, cv);
+            store_chunk(a, g, c0, cv, dot);
         }
     }
 }

@@ -326,17 +326,14 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
         const int4 sg = plan.segs[n_segs - 1 - w];
         const int64_t n = (int64_t)(sg.z - sg.y) * H;
         const float* seg = sc + (int64_t)sg.y * H;
-        float v[kSegRegs];
         float m = -INFINITY, z = 0.f;
-        for (int64_t c0 = 0; c0 < n; c0 += kWaveChunk) {
-            const int cn = (int)(n - c0 < kWaveChunk ? n - c0 : kWaveChunk);
-            const __amdgpu_buffer_rsrc_t src = span(seg + c0, (int64_t)cn * 4);
-            load_run(src, cn, lane, v);
+        // folds one chunk (cn floats in x, masked to -inf past the end) into (m, z)
+        auto fold = [&](float(&x)[kSegRegs], int cn) {
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k) {
-                if (lane >= cn - k * kWave) v[k] = -INFINITY;   // scalar bound: no per-k lane index kept
-                cm = fmaxf(cm, v[k]);
+                if (lane >= cn - k * kWave) x[k] = -INFINITY;   // scalar bound: no per-k lane index kept
+                cm = fmaxf(cm, x[k]);
             }
 #pragma unroll
             for (int o = H; o < kWave; o <<= 1) cm = fmaxf(cm, shfl_xor(cm, o));
@@ -344,10 +341,45 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
             float cz = 0.f;
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k)
-                if (k * kWave < cn) cz += exp_fast(v[k] - mn);   // exp(-inf) = 0 past the end
+                if (k * kWave < cn) cz += exp_fast(x[k] - mn);   // exp(-inf) = 0 past the end
             z = z * exp_fast(m - mn) + cz;                         // m = -inf on the first chunk: z = cz
             m = mn;
+        };
+        // floats of the chunk at c0, 0 past the end (its loads then read 0 and move no data)
+        auto chunk_len = [&](int64_t c0) {
+            return opaque_uniform((int)(n - c0 <= 0 ? 0 : (n - c0 < kWaveChunk ? n - c0 : kWaveChunk)));
+        };
+        // A chunk's kSegRegs loads, all issued: those past the chunk's end read 0 and move no data.
+        // No branch between them, so each lands in its own register of x and no copy has to wait.
+        auto load_chunk = [&](float(&x)[kSegRegs], int64_t c0, int cn) {
+            const __amdgpu_buffer_rsrc_t src = span(seg + c0, (int64_t)cn * 4);
+            const int b = opaque(lane * 4);
+#pragma unroll
+            for (int k = 0; k < kSegRegs; ++k) x[k] = bload(src, b + k * kWave * 4);
+        };
+        float v[kSegRegs];
+        int cv = chunk_len(0);
+        load_chunk(v, 0, cv);
+        if (n > kWaveChunk) {
+            // Two chunk buffers: the next chunk's loads are in flight while the current one is
+            // folded.  They are issued unconditionally (an empty chunk past the end at most), so
+            // the compiler counts them exactly and waits only for the chunk it folds.  v holds the
+            // chunk at c0 on entry to each pass.
+            float u[kSegRegs];
+            int64_t c0 = 0;
+            do {
+                const int cu = chunk_len(c0 + kWaveChunk);
+                load_chunk(u, c0 + kWaveChunk, cu);
+                __builtin_amdgcn_sched_barrier(0);   // the scheduler would sink the loads below the fold
+                fold(v, cv);
+                c0 += 2 * kWaveChunk;
+                cv = chunk_len(c0);
+                load_chunk(v, c0, cv);
+                __builtin_amdgcn_sched_barrier(0);
+                fold(u, cu);
+            } while (c0 + kWaveChunk < n);
         }
+        if (cv > 0) fold(v, cv);   // the last chunk (or the only one)
 #pragma unroll
         for (int o = H; o < kWave; o <<= 1) z += shfl_xor(z, o);
         if (sg.w >= 0) {
@@ -360,21 +392,40 @@ __global__ __launch_bounds__(kBlock) void softmax_segment_kernel(const float* sc
         }
         const float rz = 1.f / z;
         float* dseg = out + (int64_t)sg.y * H;
+        // alpha of one chunk; the stores past the chunk's end are dropped
+        auto store_chunk = [&](const float(&x)[kSegRegs], int64_t c0, int cn) {
+            const __amdgpu_buffer_rsrc_t dst = span(dseg + c0, (int64_t)cn * 4);
+            const int b = opaque(lane * 4);
+#pragma unroll
+            for (int k = 0; k < kSegRegs; ++k) bstore(dst, exp_fast(x[k] - m) * rz, b + k * kWave * 4);
+        };
         if (n <= kWaveChunk) {
-            const __amdgpu_buffer_rsrc_t dst = span(dseg, n * 4);
+            // the segment is still in registers; only the stores that hold data are issued
+            const __amdgpu_buffer_rsrc_t dst = span(dseg, (int64_t)cv * 4);
+            const int b = opaque(lane * 4);
 #pragma unroll
             for (int k = 0; k < kSegRegs; ++k)
-                if (k * kWave < n) bstore(dst, exp_fast(v[k] - m) * rz, (lane + k * kWave) * 4);
+                if (k * kWave < cv) bstore(dst, exp_fast(v[k] - m) * rz, b + k * kWave * 4);
             continue;
         }
-        for (int64_t c0 = 0; c0 < n; c0 += kWaveChunk) {
-            const int cn = (int)(n - c0 < kWaveChunk ? n - c0 : kWaveChunk);
-            const __amdgpu_buffer_rsrc_t src = span(seg + c0, (int64_t)cn * 4);
-            const __amdgpu_buffer_rsrc_t dst = span(dseg + c0, (int64_t)cn * 4);
-            load_run(src, cn, lane, v);
-#pragma unroll
-            for (int k = 0; k < kSegRegs; ++k)
-                if (k * kWave < cn) bstore(dst, exp_fast(v[k] - m) * rz, (lane + k * kWave) * 4);
+        // A longer long row is read again, pipelined as above: the next chunk's loads are in
+        // flight while the current one's alpha is computed and stored.
+        {
+            float u[kSegRegs];
+            int64_t c0 = 0;
+            cv = chunk_len(0);
+            load_chunk(v, 0, cv);
+            do {
+                const int cu = chunk_len(c0 + kWaveChunk);
+                load_chunk(u, c0 + kWaveChunk, cu);
+                __builtin_amdgcn_sched_barrier(0);
+                store_chunk(v, c0, cv);
+                c0 += 2 * kWaveChunk;
+                cv = chunk_len(c0);
+                load_chunk(v, c0, cv);
+                __builtin_amdgcn_sched_barrier(0);
+                store_chunk(u, c0 - kWaveChunk, cu);
+            } while (c0 < n);
         }
     }
 }

@@ -26,6 +26,24 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, float v, int of
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// x, with its value hidden from the optimiser at this point.  Inside a loop, the lane offsets of
+// an unrolled run are then computed from it in the loop body, where instruction selection folds
+// each constant part into the access's immediate offset.  Without it, loop-invariant code motion
+// hoists every (offset + constant) out of the loop, one VGPR each (16 of them for a 16-element
+// run), and the kernel's occupancy drops.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// The same for a wave-uniform 32-bit count (a chunk length computed from 64-bit sizes): without it
+// the compiler may keep the count 64-bit and compare it with each unrolled k * 64 as a 64-bit
+// constant, held in a VGPR pair.
+__device__ __forceinline__ int opaque_uniform(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // Loads a run of cn floats into v: v[k] = element idx + STRIDE*k (idx: the lane within a wave,
 // STRIDE 64, or the thread within a workgroup, STRIDE 256), 0 past the end.  The loads go out in
 // groups of 8 under one scalar test each, with no use of a loaded value in between, so all of
@@ -33,11 +51,12 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, float v, int of
 template <int N, int STRIDE = kWave>
 __device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t src, int cn, int idx, float (&v)[N]) {
     static_assert(N % 8 == 0, "groups of 8");
+    const int b = opaque(idx * 4);
 #pragma unroll
     for (int g = 0; g < N; g += 8) {
         if (g * STRIDE < cn) {
 #pragma unroll
-            for (int k = g; k < g + 8; ++k) v[k] = bload(src, (idx + k * STRIDE) * 4);
+            for (int k = g; k < g + 8; ++k) v[k] = bload(src, b + k * STRIDE * 4);
         } else {
 #pragma unroll
             for (int k = g; k < g + 8; ++k) v[k] = 0.f;
