@@ -114,6 +114,49 @@ struct FixSum<false> {
     __device__ static type of(float p) { return (unsigned long long)(unsigned)(p * scale); }
 };
 
+// The H values of one (row, .) slot group from LDS, 16 or 8 bytes at a time (the slots of a row are
+// consecutive and start at a multiple of H floats, so the vector reads are aligned).
+template <int H>
+__device__ __forceinline__ void read_heads(const float* p, float (&v)[H]) {
+    if constexpr (H % 4 == 0) {
+#pragma unroll
+        for (int h = 0; h < H; h += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(p + h);
+            v[h] = q.x;
+            v[h + 1] = q.y;
+            v[h + 2] = q.z;
+            v[h + 3] = q.w;
+        }
+    } else if constexpr (H == 2) {
+        const float2 q = *reinterpret_cast<const float2*>(p);
+        v[0] = q.x;
+        v[1] = q.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < H; ++h) v[h] = p[h];
+    }
+}
+
+// DPP move from the lane CTRL names; a lane whose source is outside its row, or whose row is not
+// in ROWS, receives 0 (so the values must be >= 0 for the max below).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or0(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, true);
+}
+
+// Exclusive max-scan over the wave of non-negative values (lane 0 gets 0), in registers: shifts
+// by 1, 2, 4 and 8 within each row of 16 lanes, then lane 15 of each row into the next row and
+// lane 31 into the upper two rows, then a shift of the whole wave by one lane.
+__device__ __forceinline__ int wave_max_scan_excl(int x) {
+    x = max(x, dpp_or0<0x111, 0xF>(x));   // row_shr:1
+    x = max(x, dpp_or0<0x112, 0xF>(x));   // row_shr:2
+    x = max(x, dpp_or0<0x114, 0xF>(x));   // row_shr:4
+    x = max(x, dpp_or0<0x118, 0xF>(x));   // row_shr:8
+    x = max(x, dpp_or0<0x142, 0xA>(x));   // row_bcast:15, into rows 1 and 3
+    x = max(x, dpp_or0<0x143, 0xC>(x));   // row_bcast:31, into rows 2 and 3
+    return dpp_or0<0x138, 0xF>(x);        // wave_shr:1
+}
+
 // Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per rpw (<= 32) consecutive rows, in
 // groups of consecutive such rows (whole rows, at most kBlkBudget floats).  A row of another class
 // (non-empty, deg > hi) ends a group, since its scores sit between the groups' runs.
@@ -194,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
         wave_lds_handoff();
         if (lane >= i && lane < j && deg > 0) rid_t[rb - base] = (unsigned char)(lane - i + 1);
         wave_lds_handoff();
-        // rows of this lane's edges: marks max-scanned along the edges, then over the lanes
+        // rows of this lane's edges: marks max-scanned along the edges, then over the lanes (DPP)
         int rid[EPL];
         {
             unsigned char bt[EPL];
@@ -224,14 +267,7 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 run = bt[k] > run ? bt[k] : run;
                 rid[k] = run;
             }
-            int incl = run;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int y = __shfl_up(incl, o);
-                if (lane >= o) incl = y > incl ? y : incl;
-            }
-            int excl = __shfl_up(incl, 1);
-            if (lane == 0) excl = 0;
+            const int excl = wave_max_scan_excl(run);
 #pragma unroll
             for (int k = 0; k < EPL; ++k) rid[k] = (rid[k] > excl ? rid[k] : excl) - 1;
         }
@@ -261,10 +297,11 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 const bool valid = (lane * 16 + k * H) < len;
                 const bool restart = k == 0 || rid[k] != rid[k - 1];
                 const bool lastk = k == EPL - 1 || rid[k + 1] != rid[k] || (lane * 16 + (k + 1) * H) >= len;
-                const int slot = (valid ? rid[k] : 0) * H;
+                float m[H];
+                read_heads<H>(mx + (valid ? rid[k] : 0) * H, m);
 #pragma unroll
                 for (int h = 0; h < H; ++h) {
-                    const float p = valid ? exp_fast(x[k * H + h] - mx[slot + h]) : 0.f;
+                    const float p = valid ? exp_fast(x[k * H + h] - m[h]) : 0.f;
                     x[k * H + h] = p;
                     const ZT f = Fix::of(p);
                     run[h] = restart ? f : run[h] + f;
@@ -278,8 +315,10 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
 #pragma unroll
         for (int k = 0; k < EPL; ++k) {
             const bool valid = (lane * 16 + k * H) < len;
+            float r[H];
+            read_heads<H>(rzs + (valid ? rid[k] : 0) * H, r);
 #pragma unroll
-            for (int h = 0; h < H; ++h) x[k * H + h] *= rzs[(valid ? rid[k] : 0) * H + h];
+            for (int h = 0; h < H; ++h) x[k * H + h] *= r[h];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
