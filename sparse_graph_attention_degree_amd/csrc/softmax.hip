@@ -5,7 +5,7 @@
 // The page's kernels map one thread to a (node, head) pair striding through the
 // slice with stride H, or one block per node with shared-memory reductions.
 // Here, by degree:
-//  * short rows (the common case): a wave takes 32 consecutive rows; their scores
+//  * short rows (the common case): a wave takes up to 64 consecutive rows; their scores
 //    form one contiguous run, read in groups of whole rows (up to kBlkBudget floats,
 //    16 consecutive per lane); per (row, head) maxima and sums combine through LDS
 //    atomics that are exact in any order; one HBM round trip per group of rows.
@@ -87,7 +87,12 @@ __global__ __launch_bounds__(kBlock) void softmax_short_kernel(const int32_t* __
     }
 }
 
-constexpr int kBlkRows = 32;       // rows per wave (at most: fewer on graphs too small to fill the device)
+// Rows per wave of the staged kernel (at most: fewer on graphs too small to fill the device).  64
+// halves the waves where rows are short (c5's staged rows average 1.4 edges: 1198 against 1211 us
+// for the call, c4 unchanged); at H = 16 the (row, head) tables would then take 32 KB of LDS per
+// workgroup and cut the resident waves, so it stays at 32 there.
+template <int H>
+constexpr int blk_rows() { return H >= 16 ? 32 : 64; }
 constexpr int64_t kSmFillWaves = 2048;
 constexpr int kBlkBudget = 1024;   // floats per group (whole rows), 16 per lane
 
@@ -157,7 +162,7 @@ __device__ __forceinline__ int wave_max_scan_excl(int x) {
     return dpp_or0<0x138, 0xF>(x);        // wave_shr:1
 }
 
-// Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per rpw (<= 32) consecutive rows, in
+// Rows with 0 < deg <= hi (hi * H <= kBlkBudget): a wave per rpw (<= blk_rows) consecutive rows, in
 // groups of consecutive such rows (whole rows, at most kBlkBudget floats).  A row of another class
 // (non-empty, deg > hi) ends a group, since its scores sit between the groups' runs.
 //
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
     using ZT = typename Fix::type;
     constexpr int EPL = 16 / H;                // edges per lane
     constexpr int RIDB = kBlkBudget / H;       // edges per group, at most: bytes of the row table
-    constexpr int NRH = kBlkRows * H;          // (row, head) slots
+    constexpr int NRH = blk_rows<H>() * H;     // (row, head) slots
     __shared__ __align__(16) unsigned char rid_all[kWavesPerBlock][RIDB];
     __shared__ __align__(16) float mx_all[kWavesPerBlock][NRH];          // maxima, then scale / sum
     __shared__ __align__(16) ZT z_all[kWavesPerBlock][NRH];
@@ -586,7 +591,7 @@ hipError_t launch_softmax(int H, const int32_t* row_ptr, int64_t n_rows, const f
         // Disjoint rows: the staged and slot kernels first, then the plan's segments (read from the
         // end of the table), then the hub alpha pass, which starts with the hub scores read last.
         int64_t rpw = (n_rows + kSmFillWaves - 1) / kSmFillWaves;   // enough waves to fill the device
-        rpw = rpw < 1 ? 1 : (rpw > kBlkRows ? kBlkRows : rpw);
+        rpw = rpw < 1 ? 1 : (rpw > blk_rows<HH>() ? blk_rows<HH>() : rpw);
         const int64_t bwaves = (n_rows + rpw - 1) / rpw;
         if (staged <= kZ32Rows)
             hipLaunchKernelGGL((softmax_block_kernel<HH, true>), dim3(grid_for(bwaves, kWavesPerBlock, INT32_MAX)),

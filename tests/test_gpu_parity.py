@@ -152,6 +152,23 @@ def test_edge_softmax(orc, H, sched):
     assert np.array_equal(to_np(inplace), to_np(out))
 
 
+@pytest.mark.parametrize("H", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("sched", [None, (-1, 0)], ids=str)
+def test_edge_softmax_many_rows(orc, H, sched):
+    """2^18 rows of a power-law graph (mean degree 6, cap 300, 5 % empty rows), enough rows for the
+    staged short-row kernel to take its full rows per wave (64 for H <= 8, 32 at H = 16), so many
+    short rows share a wave and its groups; without a plan the rows past the stage go to the slot
+    kernel, with the default plan to the segment kernel.  Every row against the oracle."""
+    r = np.random.default_rng(31)
+    n = 1 << 18
+    deg = G.force_zero_rows(G.degrees_powerlaw(n, 6 * n, 2.1, 300, r), 0.05, r)
+    g = G.csr_from_degrees(deg, n, r)
+    s = (r.standard_normal((g.n_edges, H)) * 3).astype(np.float32)
+    rp = to_dev(g.row_ptr)
+    out = gat.gat_edge_softmax(rp, to_dev(s), plan=_plan(rp, g.n_edges, H, 16, sched))
+    assert_close(to_np(out), orc.edge_softmax(g.row_ptr, s), "f32", "edge softmax, many rows")
+
+
 @pytest.mark.parametrize("H", [1, 4, 8, 16])
 @pytest.mark.parametrize("seg_len", [5000, 1024, 129, 100])
 def test_edge_softmax_chunk_boundaries(orc, H, seg_len):
