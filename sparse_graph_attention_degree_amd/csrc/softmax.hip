@@ -289,7 +289,13 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                 for (int h = 0; h < H; ++h) {
                     const float v = x[k * H + h];
                     run[h] = restart ? v : fmaxf(run[h], v);
-                    if (valid && lastk) atomicMax(&mx[rid[k] * H + h], run[h]);
+                }
+                // one branch for the H atomics of this edge (a branch per atomic costs more issue
+                // slots than the atomics themselves)
+                if (valid && lastk) {
+                    float* mr = mx + rid[k] * H;
+#pragma unroll
+                    for (int h = 0; h < H; ++h) atomicMax(mr + h, run[h]);
                 }
             }
         }
@@ -310,7 +316,11 @@ __global__ __launch_bounds__(kBlock) void softmax_block_kernel(const int32_t* __
                     x[k * H + h] = p;
                     const ZT f = Fix::of(p);
                     run[h] = restart ? f : run[h] + f;
-                    if (valid && lastk) atomicAdd(&zs[rid[k] * H + h], run[h]);
+                }
+                if (valid && lastk) {
+                    ZT* zr = zs + rid[k] * H;
+#pragma unroll
+                    for (int h = 0; h < H; ++h) atomicAdd(zr + h, run[h]);
                 }
             }
         }
