@@ -318,6 +318,33 @@ struct Engine {
         }
     }
 
+    // store_row for 16-bit features, through the slot's LDS row (HD floats): a lane's EPP = 8
+    // floats of a piece are 32 bytes, so stored straight from registers every instruction would
+    // write 16-byte pieces 32 bytes apart.  Each lane writes its pieces into LDS, then every
+    // instruction stores 16 bytes per lane at consecutive positions.
+    __device__ __forceinline__ void store_row_lds(float* __restrict__ out_row, float* row_lds, bool nonempty) {
+        static_assert(EPP == 8, "16-bit features");
+        wave_lds_handoff();   // the slot's reads of its previous row come before these writes
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float inv = 1.f;
+            if constexpr (MODE != kAgg) {
+                const float z = z_piece(v);
+                inv = nonempty ? 1.f / z : 0.f;
+            }
+            float4* w = reinterpret_cast<float4*>(row_lds + off[v]);
+            w[0] = make_float4(acc[v][0] * inv, acc[v][1] * inv, acc[v][2] * inv, acc[v][3] * inv);
+            w[1] = make_float4(acc[v][4] * inv, acc[v][5] * inv, acc[v][6] * inv, acc[v][7] * inv);
+        }
+        wave_lds_handoff();
+#pragma unroll
+        for (int j = 0; j < 2 * NV; ++j) {
+            const int e = (j * G + q) * 4;
+            const float4 x = *reinterpret_cast<const float4*>(row_lds + e);
+            st16(out_row + e, x.x, x.y, x.z, x.w);
+        }
+    }
+
     __device__ __forceinline__ void store_zero_row(float* __restrict__ out_row) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
@@ -402,6 +429,10 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
     const int64_t wb = wave * P * RS;
     if (wb >= n_rows) return;
     __shared__ __align__(16) float stage[kWavesPerBlock * P * E::kStage];
+    // each slot's output row, for the coalesced stores of 16-bit features
+    constexpr bool kRowLds = E::EPP == 8;
+    __shared__ __align__(16) float orow[kRowLds ? kWavesPerBlock * P * HD : 4];
+    float* my_row = orow + (kRowLds ? (threadIdx.x / kWave * P + lane / G) * HD : 0);
     const TAB vt(vf, n_src);
     const TAB kt(MODE == kLayer ? kf : vf, n_src);
     E eng;
@@ -464,7 +495,8 @@ __global__ __launch_bounds__(kBlock) void spmm_short_kernel(const int32_t* __res
         }
         if (nit != it) {
             eng.finish();
-            eng.store_row(out + (row0 + it) * HD, true);
+            if constexpr (kRowLds) eng.store_row_lds(out + (row0 + it) * HD, my_row, true);
+            else eng.store_row(out + (row0 + it) * HD, true);
             if (nit >= RS) break;
             eng.reset();
             if constexpr (MODE == kLayer) eng.set_q(qraw_n);
