@@ -44,24 +44,4 @@ __device__ __forceinline__ int opaque_uniform(int x) {
     return x;
 }
 
-// Loads a run of cn floats into v: v[k] = element idx + STRIDE*k (idx: the lane within a wave,
-// STRIDE 64, or the thread within a workgroup, STRIDE 256), 0 past the end.  The loads go out in
-// groups of 8 under one scalar test each, with no use of a loaded value in between, so all of
-// them are in flight at once.
-template <int N, int STRIDE = kWave>
-__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t src, int cn, int idx, float (&v)[N]) {
-    static_assert(N % 8 == 0, "groups of 8");
-    const int b = opaque(idx * 4);
-#pragma unroll
-    for (int g = 0; g < N; g += 8) {
-        if (g * STRIDE < cn) {
-#pragma unroll
-            for (int k = g; k < g + 8; ++k) v[k] = bload(src, b + k * STRIDE * 4);
-        } else {
-#pragma unroll
-            for (int k = g; k < g + 8; ++k) v[k] = 0.f;
-        }
-    }
-}
-
 }  // namespace gat
